@@ -1,0 +1,9 @@
+"""CPU float64 oracle for the paged KV-cache decode path (test infrastructure only).
+
+Imported by tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg;
+never by the GPU library.  See oracle/oracle.py for what it computes.
+"""
+from .oracle import (  # noqa: F401
+    BF16, F16, F32, attend, blocks_needed, decode, decode_split, gather_sequence, kv_write,
+    lse_merge, partition_state, round_to_storage, slot_to_block_offset, to_float64,
+)

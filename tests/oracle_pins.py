@@ -1,0 +1,389 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each pin takes the oracle module and raises AssertionError when the oracle
+disagrees with the pages' worked examples, a closed form, an invariant of the
+paged layout, or a pure-Python brute force written here from the textbook
+definition.  tests/test_oracle_pins.py runs every pin, and runs them all again
+against deliberately broken copies of oracle functions to show that each
+plausible mistake is caught by at least one pin.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import struct
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- helpers (independent of the oracle)
+
+def bf16_value(pattern: int) -> float:
+    return struct.unpack(">f", struct.pack(">I", (int(pattern) & 0xFFFF) << 16))[0]
+
+
+def brute_force(q, K, V, scale):
+    """Textbook softmax(q K^T scale) V with Python floats.
+
+    q: [H][D]; K, V: [L][H][D] (a never-paged, contiguous cache).  Sums use
+    math.fsum, so the result is accurate to a few float64 ulps.
+    """
+    L, H, D = len(K), len(q), len(q[0])
+    out = []
+    for h in range(H):
+        s = [scale * math.fsum(q[h][d] * K[t][h][d] for d in range(D)) for t in range(L)]
+        mx = max(s)
+        w = [math.exp(x - mx) for x in s]
+        z = math.fsum(w)
+        out.append([math.fsum(w[t] * V[t][h][d] for t in range(L)) / z for d in range(D)])
+    return out
+
+
+def place(logical, table, bs, pool):
+    """Scatter a contiguous [L, H, D] cache into pool [NB, H, bs, D] through ``table``.
+
+    Written element by element from the layout's definition: logical token t
+    sits in physical block table[t // bs] at offset t % bs.
+    """
+    L, H, D = logical.shape
+    for t in range(L):
+        b = table[t // bs]
+        for h in range(H):
+            pool[b, h, t % bs, :] = logical[t, h, :]
+
+
+class Case:
+    """A small random paged decode problem built from contiguous K/V."""
+
+    def __init__(self, rng, lens, H, D, bs, dtype="f32", pool_extra=5, scale=None, poison=True):
+        self.lens, self.H, self.D, self.bs, self.dtype = list(lens), H, D, bs, dtype
+        nblk = [-(-L // bs) for L in lens]
+        NB = sum(nblk) + pool_extra
+        perm = rng.permutation(NB)
+        M = max(nblk) + 2
+        self.tables = np.full((len(lens), M), -1, dtype=np.int32)
+        pos = 0
+        for i, n in enumerate(nblk):
+            self.tables[i, :n] = perm[pos:pos + n]
+            pos += n
+        self.scale = (1.0 / math.sqrt(D)) if scale is None else scale
+        B = len(lens)
+        if dtype == "f32":
+            self.q = rng.standard_normal((B, H, D)).astype(np.float32)
+            self.Klog = [rng.standard_normal((L, H, D)).astype(np.float32) for L in lens]
+            self.Vlog = [rng.standard_normal((L, H, D)).astype(np.float32) for L in lens]
+            fill = np.float32(np.nan) if poison else np.float32(0)
+            self.k_pool = np.full((NB, H, bs, D), fill, dtype=np.float32)
+            self.v_pool = np.full((NB, H, bs, D), fill, dtype=np.float32)
+            to_py = float
+        elif dtype == "bf16":
+            def bits(shape):
+                x = rng.standard_normal(shape).astype(np.float32)
+                return (x.view(np.uint32) >> 16).astype(np.uint16)      # truncated bf16 patterns
+            self.q = bits((B, H, D))
+            self.Klog = [bits((L, H, D)) for L in lens]
+            self.Vlog = [bits((L, H, D)) for L in lens]
+            fill = np.uint16(0x7FC0) if poison else np.uint16(0)          # bf16 quiet NaN
+            self.k_pool = np.full((NB, H, bs, D), fill, dtype=np.uint16)
+            self.v_pool = np.full((NB, H, bs, D), fill, dtype=np.uint16)
+            to_py = bf16_value
+        else:
+            raise ValueError(dtype)
+        self.to_py = to_py
+        for i in range(B):
+            place(self.Klog[i], self.tables[i], bs, self.k_pool)
+            place(self.Vlog[i], self.tables[i], bs, self.v_pool)
+        self.context_lens = np.array(lens, dtype=np.int32)
+
+    def expected(self, i):
+        f = self.to_py
+        q = [[f(x) for x in row] for row in self.q[i]]
+        K = [[[f(x) for x in r] for r in tok] for tok in self.Klog[i]]
+        V = [[[f(x) for x in r] for r in tok] for tok in self.Vlog[i]]
+        return np.array(brute_force(q, K, V, self.scale))
+
+    def run(self, o, **kw):
+        return o.decode(self.q, self.k_pool, self.v_pool, self.tables, self.context_lens, self.scale,
+                        self.bs, self.dtype, **kw)
+
+
+# ---------------------------------------------------------------- pins
+
+def pin_block_counts(o):
+    g = golden("block_counts.json")
+    bs = g["block_size"]
+    for n, nb in g["blocks"]:
+        assert o.blocks_needed(n, bs) == nb, (n, o.blocks_needed(n, bs), nb)
+    for n, empty in g["empty_slots"]:
+        assert o.blocks_needed(n, bs) * bs - n == empty
+    fr = g["four_requests"]
+    assert sum(o.blocks_needed(n, bs) for n in fr["lens"]) == fr["total_blocks"]
+    worst = max(o.blocks_needed(n, bs) * bs - n for n in range(1, 10 * bs))
+    assert worst == g["max_empty_slots"]
+
+
+def pin_storage_upcast(o):
+    g = golden("storage_bits.json")
+    for h, v in g["bf16"]:
+        got = o.to_float64(np.array([int(h, 16)], dtype=np.uint16), "bf16")[0]
+        assert got == v and math.copysign(1, got) == math.copysign(1, v), (h, got, v)
+    for h, v in g["f16"]:
+        got = o.to_float64(np.array([int(h, 16)], dtype=np.uint16), "f16")[0]
+        assert got == v, (h, got, v)
+    x = np.float32(1.0 / 3.0)
+    assert o.to_float64(np.array([x]), "f32")[0] == float(x)
+
+
+def pin_round_to_storage(o):
+    g = golden("storage_bits.json")
+    for v, h in g["bf16_round_nearest_even"]:
+        got = o.round_to_storage(np.array([v]), "bf16")[0]
+        assert got == bf16_value(int(h, 16)), (v, got, h)
+    assert o.round_to_storage(np.array([1.0 + 2.0 ** -11]), "f16")[0] == 1.0          # tie -> even
+    assert o.round_to_storage(np.array([1.0 + 3 * 2.0 ** -11]), "f16")[0] == 1.0 + 2.0 ** -9
+    assert o.round_to_storage(np.array([1.0 + 2.0 ** -30]), "f32")[0] == 1.0
+
+
+def pin_slot_example(o):
+    g = golden("slot_example.json")
+    bs, blk = g["block_size"], g["block"]
+    assert o.slot_to_block_offset(g["decode_flat_slot"], bs) == (blk, g["decode_offset"])
+    for off in g["prompt_offsets"]:
+        assert o.slot_to_block_offset(blk * bs + off, bs) == (blk, off)
+    rng = np.random.default_rng(7)
+    H, D, NB = 2, 8, 64
+    k_pool = rng.integers(0, 2 ** 16, (NB, H, bs, D), dtype=np.uint16)
+    v_pool = rng.integers(0, 2 ** 16, (NB, H, bs, D), dtype=np.uint16)
+    k = rng.integers(0, 2 ** 16, (3, H, D), dtype=np.uint16)
+    v = rng.integers(0, 2 ** 16, (3, H, D), dtype=np.uint16)
+    slots = np.array([g["decode_flat_slot"], -1, 5 * bs + 15], dtype=np.int64)
+    before = k_pool.copy()
+    k2, v2 = o.kv_write(k, v, slots, k_pool, v_pool, bs)
+    assert np.array_equal(k_pool, before)                     # inputs are not modified in place
+    exp_k, exp_v = k_pool.copy(), v_pool.copy()
+    exp_k[blk, :, g["decode_offset"], :] = k[0]
+    exp_v[blk, :, g["decode_offset"], :] = v[0]
+    exp_k[5, :, 15, :] = k[2]
+    exp_v[5, :, 15, :] = v[2]
+    assert np.array_equal(k2, exp_k) and np.array_equal(v2, exp_v)
+
+
+def pin_write_then_read(o):
+    """Writing a sequence token by token through its slots, then gathering, returns it in order."""
+    rng = np.random.default_rng(11)
+    bs, H, D, NB = 16, 3, 8, 40
+    table = rng.permutation(NB)[:4]
+    L = 53
+    toks = (rng.integers(0, 0x7F80, (L, H, D)) | (rng.integers(0, 2, (L, H, D)) << 15)).astype(np.uint16)
+    k_pool = np.full((NB, H, bs, D), 0x7FC0, dtype=np.uint16)
+    v_pool = np.full((NB, H, bs, D), 0x7FC0, dtype=np.uint16)
+    slots = np.array([int(table[t // bs]) * bs + t % bs for t in range(L)], dtype=np.int64)
+    k_pool, v_pool = o.kv_write(toks, toks[::-1].copy(), slots, k_pool, v_pool, bs)
+    back = o.gather_sequence(k_pool, table, L, bs, "bf16")
+    assert np.array_equal(back, o.to_float64(toks, "bf16").transpose(1, 0, 2))
+    backv = o.gather_sequence(v_pool, table, L, bs, "bf16")
+    assert np.array_equal(backv, o.to_float64(toks[::-1], "bf16").transpose(1, 0, 2))
+
+
+def pin_write_bitwise(o):
+    """The write moves stored bits: NaN payloads and -0.0 survive unchanged."""
+    bs, H, D, NB = 16, 1, 4, 4
+    k = np.array([[[0x7FC1, 0x8000, 0xFF81, 0x0001]]], dtype=np.uint16)
+    pool = np.zeros((NB, H, bs, D), dtype=np.uint16)
+    k2, v2 = o.kv_write(k, k, np.array([2 * bs + 3]), pool, pool, bs)
+    assert np.array_equal(k2[2, 0, 3], k[0, 0]) and np.array_equal(v2[2, 0, 3], k[0, 0])
+    f = np.array([[[np.float32(-0.0), np.float32(np.nan), 1.5, -2.0]]], dtype=np.float32)
+    poolf = np.ones((NB, H, bs, D), dtype=np.float32)
+    k3, _ = o.kv_write(f, f, np.array([7]), poolf, poolf, bs)
+    assert np.array_equal(k3[0, 0, 7].view(np.uint32), f[0, 0].view(np.uint32))
+
+
+def pin_brute_force(o):
+    """The paged oracle equals the textbook formula on never-paged K/V."""
+    rng = np.random.default_rng(1234)
+    cases = [
+        Case(rng, [6, 50, 8, 100], H=4, D=64, bs=16),                      # the pages' four requests
+        Case(rng, [1, 16, 17, 33], H=2, D=8, bs=16, scale=0.37),
+        Case(rng, [31, 5, 64], H=3, D=16, bs=32, dtype="bf16"),
+        Case(rng, [2, 40], H=2, D=4, bs=16, scale=2.5),
+    ]
+    for c in cases:
+        got = c.run(o)
+        for i in range(len(c.lens)):
+            exp = c.expected(i)
+            assert np.max(np.abs(got[i] - exp)) <= 1e-12 * max(1.0, np.max(np.abs(exp))), (c.lens, i)
+
+
+def pin_pages_tables(o):
+    """The pages' example tables, read in place, give the textbook result."""
+    g = golden("tables.json")
+    rng = np.random.default_rng(5)
+    H, D, bs = 2, 8, 16
+    tabs = [g["card"]["table"], g["step5_request_b"]["table"]] + list(g["memory_usage"]["tables"].values())
+    lens = [40, 35, 9, 37, 16]
+    NB = 100
+    B = len(tabs)
+    tables = np.full((B, 4), -1, dtype=np.int32)
+    k_pool = np.full((NB, H, bs, D), np.nan, dtype=np.float32)
+    v_pool = np.full((NB, H, bs, D), np.nan, dtype=np.float32)
+    q = rng.standard_normal((B, H, D)).astype(np.float32)
+    Ks, Vs = [], []
+    assert len(set(sum(tabs, []))) == sum(len(t) for t in tabs)      # the examples' ids are disjoint
+    for i, (t, L) in enumerate(zip(tabs, lens)):
+        assert len(t) == -(-L // bs)
+        tables[i, :len(t)] = t
+        K = rng.standard_normal((L, H, D)).astype(np.float32)
+        V = rng.standard_normal((L, H, D)).astype(np.float32)
+        place(K, t, bs, k_pool)
+        place(V, t, bs, v_pool)
+        Ks.append(K)
+        Vs.append(V)
+    lens_a = np.array(lens, dtype=np.int32)
+    got = o.decode(q, k_pool, v_pool, tables, lens_a, 0.5, bs, "f32")
+    for i in range(B):
+        exp = np.array(brute_force(q[i].astype(float).tolist(), Ks[i].astype(float).tolist(),
+                                   Vs[i].astype(float).tolist(), 0.5))
+        assert np.max(np.abs(got[i] - exp)) <= 1e-12
+
+
+def pin_permutation_invariance(o):
+    """Relabelling physical blocks (moving them and rewriting tables) changes nothing, bit for bit."""
+    rng = np.random.default_rng(99)
+    c = Case(rng, [6, 50, 8, 100, 1], H=4, D=16, bs=16, pool_extra=20)
+    base = c.run(o)
+    NB = c.k_pool.shape[0]
+    for _ in range(3):
+        pi = rng.permutation(NB)
+        kp = np.empty_like(c.k_pool)
+        vp = np.empty_like(c.v_pool)
+        kp[pi] = c.k_pool
+        vp[pi] = c.v_pool
+        tabs = np.where(c.tables >= 0, pi[np.maximum(c.tables, 0)], -1).astype(np.int32)
+        got = o.decode(c.q, kp, vp, tabs, c.context_lens, c.scale, c.bs, c.dtype)
+        assert np.array_equal(got, base)
+
+
+def pin_poison_invariance(o):
+    """Slots past L, blocks in no table and table padding never reach the output."""
+    rng = np.random.default_rng(3)
+    clean = Case(np.random.default_rng(3), [6, 50, 8, 100], H=2, D=8, bs=16, poison=False)
+    dirty = Case(rng, [6, 50, 8, 100], H=2, D=8, bs=16, poison=True)
+    a, b = clean.run(o), dirty.run(o)
+    assert np.all(np.isfinite(b)) and np.array_equal(a, b)
+    tabs = dirty.tables.copy()
+    tabs[tabs < 0] = 10 ** 6                       # padding that would be out of range if read
+    c = o.decode(dirty.q, dirty.k_pool, dirty.v_pool, tabs, dirty.context_lens, dirty.scale, 16, "f32")
+    assert np.array_equal(c, b)
+
+
+def pin_closed_forms(o):
+    rng = np.random.default_rng(21)
+    bs, H, D = 16, 3, 8
+    # one token: the output is that token's V row exactly
+    c = Case(rng, [1, 1], H=H, D=D, bs=bs, scale=1.7)
+    got = c.run(o)
+    for i in range(2):
+        assert np.array_equal(got[i], c.Vlog[i][0].astype(np.float64))
+    # q = 0 (or scale = 0): the mean of V over the context
+    c = Case(rng, [37, 5], H=H, D=D, bs=bs)
+    c.q[:] = 0
+    got = c.run(o)
+    for i in range(2):
+        assert np.allclose(got[i], c.Vlog[i].astype(np.float64).mean(axis=0), rtol=0, atol=1e-14)
+    # a constant V row is returned unchanged
+    c = Case(rng, [29], H=H, D=D, bs=bs)
+    c.Vlog[0][:] = np.float32(0.625)
+    place(c.Vlog[0], c.tables[0], bs, c.v_pool)
+    assert np.allclose(c.run(o)[0], 0.625, rtol=0, atol=1e-15)
+    # two tokens: sigmoid weights
+    c = Case(rng, [2], H=1, D=4, bs=bs, scale=0.8)
+    q = c.q[0, 0].astype(float)
+    k0, k1 = c.Klog[0][0, 0].astype(float), c.Klog[0][1, 0].astype(float)
+    v0, v1 = c.Vlog[0][0, 0].astype(float), c.Vlog[0][1, 0].astype(float)
+    s0, s1 = 0.8 * math.fsum(q * k0), 0.8 * math.fsum(q * k1)
+    w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    assert np.allclose(c.run(o)[0, 0], w0 * v0 + (1 - w0) * v1, rtol=0, atol=1e-14)
+    # hand example: scores 1, 0, -1 -> weights e, 1, 1/e
+    q = np.array([[[1, 0]]], dtype=np.float32)
+    kp = np.zeros((2, 1, bs, 2), dtype=np.float32)
+    vp = np.zeros((2, 1, bs, 2), dtype=np.float32)
+    kp[1, 0, :3] = [[1, 0], [0, 1], [-1, 0]]
+    vp[1, 0, :3] = [[1, 0], [0, 1], [0, 0]]
+    got = o.decode(q, kp, vp, np.array([[1]], dtype=np.int32), np.array([3]), 1.0, bs, "f32")
+    z = math.e + 1 + 1 / math.e
+    assert np.allclose(got[0, 0], [math.e / z, 1 / z], rtol=0, atol=1e-15)
+    # linearity in V and scale folding
+    c = Case(rng, [45, 17], H=H, D=D, bs=bs)
+    a = c.run(o)
+    c2 = Case(np.random.default_rng(0), [45, 17], H=H, D=D, bs=bs)
+    c2.q, c2.k_pool, c2.tables, c2.scale = c.q, c.k_pool, c.tables, c.scale
+    c.v_pool = (np.round(c.v_pool * 256) / 256).astype(np.float32)      # exact under the maps below
+    a = c.run(o)
+    c2.v_pool = np.where(np.isnan(c.v_pool), np.nan, -2.0 * c.v_pool + 0.5).astype(np.float32)
+    assert np.allclose(c2.run(o), -2.0 * a + 0.5, rtol=0, atol=1e-12)
+    c3 = Case(np.random.default_rng(0), [45, 17], H=H, D=D, bs=bs)
+    c3.q, c3.k_pool, c3.v_pool, c3.tables = c.q * np.float32(2.0), c.k_pool, c.v_pool, c.tables
+    c3.scale = c.scale / 2.0
+    assert np.allclose(c3.run(o), a, rtol=0, atol=1e-13)
+    # empty context: zero row
+    c = Case(rng, [4, 9], H=H, D=D, bs=bs)
+    c.context_lens[0] = 0
+    got = c.run(o)
+    assert np.array_equal(got[0], np.zeros((H, D)))
+
+
+def pin_split_equals_single(o):
+    """Partitioned evaluation with a log-sum-exp merge equals the one-pass result."""
+    rng = np.random.default_rng(8)
+    for lens, bs, parts in (([6, 50, 8, 100], 16, (16, 32, 48, 512)),
+                            ([700, 33, 1024], 16, (64, 256, 512)),
+                            ([95, 400], 32, (32, 64, 128))):
+        c = Case(rng, lens, H=2, D=8, bs=bs)
+        one = c.run(o)
+        for P in parts:
+            sp = o.decode_split(c.q, c.k_pool, c.v_pool, c.tables, c.context_lens, c.scale, bs, c.dtype, P)
+            assert np.max(np.abs(sp - one)) <= 1e-12, (lens, P)
+    # widely different partition maxima still merge correctly
+    c = Case(rng, [64], H=1, D=4, bs=16, scale=1.0)
+    c.Klog[0][:32] *= 30
+    place(c.Klog[0], c.tables[0], 16, c.k_pool)
+    ref = c.expected(0)
+    sp = o.decode_split(c.q, c.k_pool, c.v_pool, c.tables, c.context_lens, 1.0, 16, "f32", 16)
+    assert np.max(np.abs(sp[0] - ref)) <= 1e-12
+
+
+def pin_prefix_sharing(o):
+    """Tables that share a physical block equal the same data duplicated into private blocks."""
+    g = golden("tables.json")["prefix_sharing"]
+    rng = np.random.default_rng(4)
+    bs, H, D, NB = 16, 2, 8, 80
+    tabs = list(g["tables"].values())
+    shared = g["shared_block"]
+    lens = [bs + 3, bs + 11, bs + 16]
+    k_pool = rng.standard_normal((NB, H, bs, D)).astype(np.float32)
+    v_pool = rng.standard_normal((NB, H, bs, D)).astype(np.float32)
+    q = rng.standard_normal((3, H, D)).astype(np.float32)
+    tables = np.array(tabs, dtype=np.int32)
+    a = o.decode(q, k_pool, v_pool, tables, np.array(lens), 0.3, bs, "f32")
+    private = [70, 71, 72]
+    tables2 = tables.copy()
+    for i, p in enumerate(private):
+        k_pool[p] = k_pool[shared]
+        v_pool[p] = v_pool[shared]
+        tables2[i, 0] = p
+    b = o.decode(q, k_pool, v_pool, tables2, np.array(lens), 0.3, bs, "f32")
+    assert np.array_equal(a, b)
+
+
+PINS = [pin_block_counts, pin_storage_upcast, pin_round_to_storage, pin_slot_example,
+        pin_write_then_read, pin_write_bitwise, pin_brute_force, pin_pages_tables,
+        pin_permutation_invariance, pin_poison_invariance, pin_closed_forms,
+        pin_split_equals_single, pin_prefix_sharing]

@@ -1,0 +1,163 @@
+"""The CPU oracle against its pins, and the pins against planted mistakes.
+
+Every pin in oracle_pins.PINS must pass on the oracle as committed.  Then each
+plausible mistake below is planted in a copy of one oracle function (on the
+CPU, by monkeypatching the oracle module) and at least one pin must fail.
+"""
+import numpy as np
+import pytest
+
+import oracle.oracle as O
+import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(O)
+
+
+# ------------------------------------------------------------- planted mistakes
+
+def _floor_blocks(n, bs):
+    return int(n) // int(bs)
+
+
+def _gather_no_transpose(cache, table_row, num_tokens, block_size, dtype):
+    nb = O.blocks_needed(num_tokens, block_size)
+    blocks = O.to_float64(np.asarray(cache)[np.asarray(table_row[:nb])], dtype)
+    H, D = blocks.shape[1], blocks.shape[3]
+    return blocks.reshape(H, nb * block_size, D)[:, :num_tokens, :]
+
+
+def _gather_shifted_table(cache, table_row, num_tokens, block_size, dtype):
+    nb = O.blocks_needed(num_tokens, block_size)
+    row = np.asarray(table_row)
+    ids = np.concatenate([row[1:nb + 1], row[:1]])[:nb]
+    blocks = O.to_float64(np.asarray(cache)[ids], dtype)
+    H, D = blocks.shape[1], blocks.shape[3]
+    return blocks.transpose(1, 0, 2, 3).reshape(H, nb * block_size, D)[:, :num_tokens, :]
+
+
+def _attend_no_scale(q, K, V, scale):
+    s = np.einsum("hd,htd->ht", q, K)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    return np.einsum("ht,htd->hd", p, V) / p.sum(axis=1)[:, None]
+
+
+def _attend_neg_exp(q, K, V, scale):
+    s = np.einsum("hd,htd->ht", q, K) * scale
+    p = np.exp(-(s - s.max(axis=1, keepdims=True)))
+    return np.einsum("ht,htd->hd", p, V) / p.sum(axis=1)[:, None]
+
+
+def _attend_unnormalised(q, K, V, scale):
+    s = np.einsum("hd,htd->ht", q, K) * scale
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    return np.einsum("ht,htd->hd", p, V)
+
+
+def _attend_swapped_kv(q, K, V, scale):
+    return O.__dict__["_orig_attend"](q, V, K, scale)
+
+
+def _upcast_wrong_shift(storage, dtype):
+    if dtype == "bf16":
+        bits = np.asarray(storage).view(np.uint16).astype(np.uint32) << np.uint32(8)
+        return bits.view(np.float32).astype(np.float64)
+    return O.__dict__["_orig_to_float64"](storage, dtype)
+
+
+def _slot_swapped(slot, bs):
+    return slot % bs, slot // bs
+
+
+def _merge_unweighted(states):
+    num = sum(acc for _, _, acc in states)
+    den = sum(l for _, l, _ in states)
+    return num / den[:, None]
+
+
+def _merge_wrong_sign(states):
+    M = np.max(np.stack([m for m, _, _ in states]), axis=0)
+    num = sum(np.exp(M - m)[:, None] * acc for m, _, acc in states)
+    den = sum(np.exp(M - m) * l for m, l, _ in states)
+    return num / den[:, None]
+
+
+def _state_no_scale(q, K, V, scale):
+    return O.__dict__["_orig_partition_state"](q, K, V, 1.0)
+
+
+def _round_truncate(x, dtype):
+    if dtype == "bf16":
+        u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32) >> 16
+        return O.to_float64(u.astype(np.uint16), "bf16")
+    return O.__dict__["_orig_round_to_storage"](x, dtype)
+
+
+def _decode_skip_last(q, k_cache, v_cache, block_tables, context_lens, scale, block_size, dtype, seqs=None):
+    B = np.asarray(q).shape[0]
+    return O.__dict__["_orig_decode"](q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                                      dtype, seqs=range(B - 1) if seqs is None else seqs)
+
+
+def _decode_short_context(q, k_cache, v_cache, block_tables, context_lens, scale, block_size, dtype, seqs=None):
+    lens = np.maximum(np.asarray(context_lens) - 1, 1)
+    return O.__dict__["_orig_decode"](q, k_cache, v_cache, block_tables, lens, scale, block_size, dtype,
+                                      seqs=seqs)
+
+
+def _write_skips_token0(k, v, slot_mapping, k_cache, v_cache, block_size):
+    sm = np.array(slot_mapping, copy=True)
+    sm[0] = -1
+    return O.__dict__["_orig_kv_write"](k, v, sm, k_cache, v_cache, block_size)
+
+
+def _write_swaps_kv(k, v, slot_mapping, k_cache, v_cache, block_size):
+    return O.__dict__["_orig_kv_write"](v, k, slot_mapping, k_cache, v_cache, block_size)
+
+
+def _write_ignores_padding(k, v, slot_mapping, k_cache, v_cache, block_size):
+    # forgets that a negative slot means "no write" (Python's negative indexing then hits the last block)
+    k_out, v_out = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    for t, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        b, o = slot // block_size, slot % block_size
+        k_out[b, :, o, :] = k[t]
+        v_out[b, :, o, :] = v[t]
+    return k_out, v_out
+
+
+MUTANTS = {
+    "blocks_needed floors": ("blocks_needed", _floor_blocks),
+    "gather drops the head transpose": ("gather_sequence", _gather_no_transpose),
+    "gather reads the next table entry": ("gather_sequence", _gather_shifted_table),
+    "attend drops the scale": ("attend", _attend_no_scale),
+    "attend negates the exponent": ("attend", _attend_neg_exp),
+    "attend skips the normalisation": ("attend", _attend_unnormalised),
+    "attend swaps K and V": ("attend", _attend_swapped_kv),
+    "bf16 upcast shifts by 8": ("to_float64", _upcast_wrong_shift),
+    "slot decoding swaps block and offset": ("slot_to_block_offset", _slot_swapped),
+    "merge forgets the LSE weights": ("lse_merge", _merge_unweighted),
+    "merge weights with the wrong sign": ("lse_merge", _merge_wrong_sign),
+    "partition state drops the scale": ("partition_state", _state_no_scale),
+    "bf16 rounding truncates": ("round_to_storage", _round_truncate),
+    "decode skips the last sequence": ("decode", _decode_skip_last),
+    "decode reads one token too few": ("decode", _decode_short_context),
+    "write drops a token": ("kv_write", _write_skips_token0),
+    "write swaps K and V": ("kv_write", _write_swaps_kv),
+    "write ignores negative-slot padding": ("kv_write", _write_ignores_padding),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, bad = MUTANTS[name]
+    monkeypatch.setitem(O.__dict__, "_orig_" + attr, getattr(O, attr))
+    monkeypatch.setattr(O, attr, bad)
+    failed = []
+    for pin in P.PINS:
+        try:
+            pin(O)
+        except Exception:          # an assertion, or the mistake breaking the computation outright
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches: {name}"
