@@ -1,0 +1,148 @@
+/*
+ * pagedkv.h -- C ABI of a paged KV-cache decode library for AMD MI355X (gfx950).
+ *
+ * Sources (web pages on vLLM's PagedAttention):
+ *   [card]    "PagedAttention", llm-engineer.pages.dev
+ *   [explain] "vLLM KV cache and PagedAttention explained", hrletsgo.me
+ *   [velog]   "vLLM의 PagedAttention 아키텍처와 GPU 메모리 최적화 원리", velog.io
+ *
+ * Cache layout.  K and V are two separate, contiguous pools of fixed-size
+ * physical blocks, each laid out [num_blocks, num_heads, block_size, head_dim]
+ * ([velog] section 4, the 4-D layout [Block, Head, Block_Size, Head_D]).  One
+ * (block, head) tile of block_size * head_dim elements is contiguous, so a
+ * block is read as whole coalesced rows ([card] "Kernel은 무엇이 달라지는가":
+ * the scatter is per block, not per token).
+ *
+ * Block tables.  Row i of block_tables (int32, [num_seqs, max_blocks_per_seq],
+ * row-major) lists the physical blocks of sequence i: entry j holds logical
+ * tokens j*block_size .. j*block_size + block_size - 1 ([card] "OS paging과
+ * 같은 발상"; [explain] Step 5).  A sequence of L tokens uses the first
+ * ceil(L / block_size) entries ([explain] Step 6); later entries are never
+ * read.  One physical block may appear in several rows (read-only prefix
+ * sharing, [explain] Step 9).
+ *
+ * Slot mapping.  slot = block * block_size + offset names offset `offset` of
+ * physical block `block` ("slot 6 of block 42", [explain] Steps 6-7); a
+ * negative slot means "no write".
+ *
+ * Element types.  q, the caches and out share one type: PKV_F32, PKV_F16 or
+ * PKV_BF16.  Arithmetic is fp32 throughout; out is rounded to nearest even.
+ * Supported shapes: head_dim 64 or 128, block_size 16 or 32.
+ *
+ * Pointers and ownership.  Every array argument is a DEVICE pointer to memory
+ * the caller allocated and owns; the library allocates nothing, keeps no state
+ * between calls and never retains a pointer.  `stream` is a hipStream_t passed
+ * as void* (NULL = the legacy default stream).  All work is enqueued
+ * asynchronously on `stream`; nothing synchronises with the host except in
+ * PKV_DEBUG mode (below).  Outputs must not alias inputs.
+ *
+ * Errors.  Every call validates its scalar arguments and pointers on the host
+ * before any HIP call; on failure it returns a non-zero pkv_status, launches
+ * nothing and leaves a message for pkv_last_error().  A failed launch returns
+ * PKV_EHIP.  Faults inside a kernel surface at the caller's next
+ * synchronisation, as for any HIP kernel.
+ *
+ * Caller contract on metadata (device data the host does not read): block ids
+ * in [0, num_blocks), 0 <= context_lens[i] <= max_blocks_per_seq*block_size,
+ * no two non-negative equal slots in one write.  The kernels never read or
+ * write outside the arrays when it is broken: an out-of-range block id or
+ * context length turns that sequence's output rows into NaN, and a slot whose
+ * block is out of range is not written.  With the environment variable
+ * PKV_DEBUG=1 each call also copies the metadata to the host, synchronising
+ * `stream`, and returns PKV_EINVAL naming the first violation.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,        /* bad argument: null pointer, negative or inconsistent size      */
+  PKV_EUNSUPPORTED = 2,  /* valid but not built: dtype, head_dim, block_size, grid too big */
+  PKV_EWORKSPACE = 3,    /* workspace missing or smaller than paged_attention_workspace_bytes */
+  PKV_EHIP = 4           /* the HIP runtime refused a launch or a copy                      */
+} pkv_status;
+
+/*
+ * paged_kv_write -- store each new token's K and V rows in its cache slot.
+ *
+ * For every t in [0, num_tokens) with s = slot_mapping[t] >= 0:
+ *   k_cache[s / block_size, h, s % block_size, :] = k[t, h, :]   for all heads h
+ *   v_cache[...same...]                           = v[t, h, :]
+ * This is the decode step's append of the new token's K/V into the next slot
+ * of its sequence's last block ([explain] Step 6: "stored in slot 6 of block
+ * 42"; [card] "vLLM에서의 위치": the worker prepares the slot mapping).  The
+ * copy moves stored bits and is exact.
+ *
+ *   k, v          [num_tokens, num_heads, head_dim], dtype, contiguous, read
+ *   slot_mapping  [num_tokens] int64, read
+ *   k_cache,
+ *   v_cache       [num_blocks, num_heads, block_size, head_dim], dtype, written
+ *                 only at the named slots
+ * Returns PKV_OK, or an error status with nothing launched.  num_tokens == 0
+ * is a no-op.
+ */
+int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64_t num_tokens,
+                   void* k_cache, void* v_cache, int64_t num_blocks, int32_t num_heads,
+                   int32_t head_dim, int32_t block_size, int32_t dtype, void* stream);
+
+/*
+ * paged_attention_workspace_bytes -- device scratch that paged_attention_decode
+ * needs for its split-context partials with these sizes (0 when no sequence
+ * can span more than one partition).  Returns 0 for invalid sizes as well;
+ * paged_attention_decode reports those.
+ */
+size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                       int32_t max_blocks_per_seq, int32_t block_size,
+                                       int32_t partition_size);
+
+/*
+ * paged_attention_decode -- one query token per sequence attends over that
+ * sequence's paged K/V cache, read in place through its block table.
+ *
+ * For each sequence i with L = context_lens[i] and each head h:
+ *   out[i, h, :] = softmax_t( scale * q[i, h, :] . K_i[t, h, :] ) V_i[t, h, :],  t in [0, L)
+ * where K_i[t] = k_cache[block_tables[i, t / block_size], :, t % block_size, :]
+ * and likewise V_i ([explain] Appendix: Attention(Q,K,V) = softmax(QK^T/sqrt(d))V,
+ * evaluated by walking the block table one block at a time with a running
+ * softmax normalisation).  Rows with L == 0 are zero.
+ *
+ * Long contexts are split into partitions of partition_size tokens, each
+ * reduced independently and then merged by log-sum-exp weights; the result is
+ * the same softmax (the pages name this FlashDecoding, [card] "헷갈리기 쉬운 구분").
+ * partition_size must be a multiple of block_size; 0 means never split.
+ *
+ *   q             [num_seqs, num_heads, head_dim], dtype, read
+ *   k_cache,
+ *   v_cache       [num_blocks, num_heads, block_size, head_dim], dtype, read
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32, read
+ *   context_lens  [num_seqs] int32, read
+ *   out           [num_seqs, num_heads, head_dim], dtype, written
+ *   workspace     >= paged_attention_workspace_bytes(...) bytes of device memory,
+ *                 used as scratch (may be NULL when that is 0); no initial
+ *                 contents needed; must not be shared by concurrent calls
+ * Returns PKV_OK, or an error status with nothing launched.
+ */
+int paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                           int32_t dtype, void* out, void* workspace, size_t workspace_bytes,
+                           int32_t partition_size, void* stream);
+
+/* Text of the calling thread's last non-OK status (empty string if none). */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,189 @@
+// C-ABI front end: host-side validation, workspace sizing, dispatch and the
+// optional metadata checks.  No HIP call happens before validation succeeds.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "pagedkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PKV_OK;
+}
+
+bool debug_checks() {
+  const char* e = getenv("PKV_DEBUG");
+  return e != nullptr && e[0] == '1';
+}
+
+int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : 2; }
+
+// Shared shape checks of both calls.
+int check_shape(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                int64_t num_blocks) {
+  if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16)
+    return fail(PKV_EUNSUPPORTED, "dtype %d is not PKV_F32, PKV_F16 or PKV_BF16", dtype);
+  if (num_heads <= 0) return fail(PKV_EINVAL, "num_heads must be positive (got %d)", num_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (block_size != 16 && block_size != 32)
+    return fail(PKV_EUNSUPPORTED, "block_size %d not supported (16 or 32)", block_size);
+  if (num_blocks <= 0) return fail(PKV_EINVAL, "num_blocks must be positive (got %lld)", (long long)num_blocks);
+  // every byte offset into a cache pool must fit in int64
+  const double pool_bytes = double(num_blocks) * num_heads * block_size * head_dim * elem_bytes(dtype);
+  if (pool_bytes > 4.0e18) return fail(PKV_EINVAL, "cache pool of %.3g bytes is too large", pool_bytes);
+  return PKV_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Partitions the grid spans: ceil(max_blocks / part_blocks).
+int64_t partitions_for(int32_t max_blocks, int32_t part_blocks) {
+  return (int64_t(max_blocks) + part_blocks - 1) / part_blocks;
+}
+
+int32_t part_blocks_for(int32_t max_blocks, int32_t block_size, int32_t partition_size) {
+  return partition_size == 0 ? max_blocks : partition_size / block_size;
+}
+
+}  // namespace
+
+extern "C" const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                                  int32_t head_dim, int32_t max_blocks_per_seq,
+                                                  int32_t block_size, int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+      block_size <= 0 || partition_size < 0 || partition_size % block_size != 0)
+    return 0;
+  const int32_t pb = part_blocks_for(max_blocks_per_seq, block_size, partition_size);
+  return pkv::workspace_layout(num_seqs, num_heads, head_dim, partitions_for(max_blocks_per_seq, pb)).bytes;
+}
+
+extern "C" int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping,
+                              int64_t num_tokens, void* k_cache, void* v_cache, int64_t num_blocks,
+                              int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+                              void* stream) {
+  if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens must be >= 0 (got %lld)", (long long)num_tokens);
+  if (int rc = check_shape(dtype, num_heads, head_dim, block_size, num_blocks)) return rc;
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return fail(PKV_EINVAL, "null pointer among k, v, slot_mapping, k_cache, v_cache");
+  const int64_t vecs = num_tokens * int64_t(num_heads) * (head_dim * elem_bytes(dtype) / 16);
+  if (vecs / 256 >= (int64_t(1) << 31) - 1) return fail(PKV_EUNSUPPORTED, "num_tokens %lld too large for one launch", (long long)num_tokens);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    std::vector<int64_t> slots(num_tokens);
+    hipError_t e = hipMemcpyAsync(slots.data(), slot_mapping, num_tokens * sizeof(int64_t), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "PKV_DEBUG copy of slot_mapping");
+    std::unordered_set<int64_t> seen;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+      const int64_t s = slots[t];
+      if (s < 0) continue;
+      if (s / block_size >= num_blocks)
+        return fail(PKV_EINVAL, "slot_mapping[%lld] = %lld names block %lld >= num_blocks %lld", (long long)t,
+                    (long long)s, (long long)(s / block_size), (long long)num_blocks);
+      if (!seen.insert(s).second)
+        return fail(PKV_EINVAL, "slot_mapping[%lld] = %lld repeats an earlier slot", (long long)t, (long long)s);
+    }
+  }
+  hipError_t e = pkv::launch_kv_write(dtype, head_dim, k, v, slot_mapping, num_tokens, k_cache, v_cache,
+                                      num_blocks, num_heads, block_size, st);
+  if (e != hipSuccess) return hip_fail(e, "paged_kv_write launch");
+  return ok();
+}
+
+extern "C" int paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                      float scale, int32_t dtype, void* out, void* workspace,
+                                      size_t workspace_bytes, int32_t partition_size, void* stream) {
+  if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (int rc = check_shape(dtype, num_heads, head_dim, block_size, num_blocks)) return rc;
+  if (max_blocks_per_seq <= 0)
+    return fail(PKV_EINVAL, "max_blocks_per_seq must be positive (got %d)", max_blocks_per_seq);
+  if (int64_t(max_blocks_per_seq) * block_size > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "table capacity of %lld tokens exceeds int32", (long long)max_blocks_per_seq * block_size);
+  if (partition_size < 0 || partition_size % block_size != 0)
+    return fail(PKV_EINVAL, "partition_size %d must be 0 or a positive multiple of block_size %d",
+                partition_size, block_size);
+  if (!isfinite(scale)) return fail(PKV_EINVAL, "scale must be finite");
+  if (num_seqs == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return fail(PKV_EINVAL, "null pointer among q, k_cache, v_cache, block_tables, context_lens, out");
+  if (num_heads > 65535 || num_seqs > 65535)
+    return fail(PKV_EUNSUPPORTED, "num_heads %d / num_seqs %d exceed the grid limit 65535", num_heads, num_seqs);
+  const int32_t pb = part_blocks_for(max_blocks_per_seq, block_size, partition_size);
+  const int64_t parts = partitions_for(max_blocks_per_seq, pb);
+  if (parts > 65535) return fail(PKV_EUNSUPPORTED, "%lld partitions exceed the grid limit 65535", (long long)parts);
+  const pkv::WorkspaceLayout wl = pkv::workspace_layout(num_seqs, num_heads, head_dim, parts);
+  if (wl.bytes > 0 && (workspace == nullptr || workspace_bytes < wl.bytes))
+    return fail(PKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given%s", wl.bytes, workspace_bytes,
+                workspace ? "" : " (null)");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    std::vector<int32_t> lens(num_seqs), tab(size_t(num_seqs) * max_blocks_per_seq);
+    hipError_t e = hipMemcpyAsync(lens.data(), context_lens, lens.size() * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(tab.data(), block_tables, tab.size() * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "PKV_DEBUG copy of metadata");
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      const int64_t L = lens[i];
+      if (L < 0 || L > int64_t(max_blocks_per_seq) * block_size)
+        return fail(PKV_EINVAL, "context_lens[%d] = %lld outside [0, %lld]", i, (long long)L,
+                    (long long)max_blocks_per_seq * block_size);
+      for (int64_t j = 0; j < (L + block_size - 1) / block_size; ++j) {
+        const int32_t b = tab[size_t(i) * max_blocks_per_seq + j];
+        if (b < 0 || b >= num_blocks)
+          return fail(PKV_EINVAL, "block_tables[%d, %lld] = %d outside [0, %lld)", i, (long long)j, b,
+                      (long long)num_blocks);
+      }
+    }
+  }
+  pkv::DecodeArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_m = wl.bytes ? reinterpret_cast<float*>(ws + wl.m_off) : nullptr;
+  a.ws_l = wl.bytes ? reinterpret_cast<float*>(ws + wl.l_off) : nullptr;
+  a.ws_acc = wl.bytes ? reinterpret_cast<float*>(ws + wl.acc_off) : nullptr;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.part_blocks = pb;
+  a.partitions = int32_t(parts);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = pkv::launch_decode(dtype, head_dim, block_size, a, st);
+  if (e != hipSuccess) return hip_fail(e, "paged_attention_decode launch");
+  return ok();
+}

@@ -1,0 +1,401 @@
+// Paged-attention decode for gfx950: one query token per sequence attends
+// over its K/V cache, read in place through the sequence's block table.
+//
+// What is computed ("vLLM KV cache and PagedAttention explained", hrletsgo.me,
+// Appendix: The Attention Score Formula): out = softmax(q K^T * scale) V over
+// the sequence's first L cached tokens, evaluated by walking the block table
+// one block at a time, scoring the block's keys, updating a running softmax
+// normalisation and accumulating the weighted values.  Blocks are read where
+// they are, never compacted ("PagedAttention" card, section "Kernel은 무엇이
+// 달라지는가").  Long contexts are cut into partitions that are reduced
+// independently and merged by log-sum-exp weights (the card names this
+// FlashDecoding in "헷갈리기 쉬운 구분").
+//
+// Work decomposition.  One work-group of 4 wave64s per (head, partition,
+// sequence); the grid's fastest index is the head, so work-groups running
+// together read neighbouring (block, head) tiles of the same physical blocks.
+// Wave w of a partition takes its blocks w, w+4, w+8, ...
+//
+// Data movement.  A (block, head) tile of K is block_size * head_dim elements
+// in one contiguous run ("vLLM의 PagedAttention 아키텍처와 GPU 메모리 최적화 원리",
+// velog, section 4 layout).  A token row is 256 B for every supported
+// shape except 16-bit head_dim 64 (128 B), so a wave-wide 16 B-per-lane load
+// moves 1 KiB = 4 whole rows, perfectly coalesced.  Each lane keeps the 16 B
+// it loaded and uses them itself (its q slice is the same 16 B column), so
+// tiles go straight from HBM to VGPRs: there is no cross-lane reuse for an LDS
+// round trip to serve.  Loads use a buffer resource sized to the tile's valid
+// rows: rows past the context end (and the whole tile of an invalid block id)
+// read as zero without touching memory.  Two tile buffers per wave keep the
+// next block's K and V in flight while the current one is consumed.
+//
+// Arithmetic.  q.k uses the packed dot2 instructions for 16-bit types (exact
+// products, fp32 sums) and fp32 FMA for fp32; each row's partial dots are
+// summed across its 8/16/32 lanes with DPP.  The 16 lanes of a row then hold
+// identical scores, so every token row of a wave (4 per load) keeps its own
+// running (max, sum, acc) state in registers with no cross-row traffic in the
+// loop; rows and waves are merged once at the end through LDS.  Scores are
+// base-2 logits (scale * log2 e folded in) so exp is a single v_exp_f32.
+#include <hip/hip_fp16.h>
+
+#include "pagedkv.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+// Running max before any token is seen.  Finite, so 2^(m - m') is defined
+// while a row has seen only masked tokens; any real score exceeds it.
+constexpr float kEmptyMax = -3.0e38f;
+// Word 3 of a gfx9 raw buffer resource: 32-bit data format, no swizzle.
+constexpr int kBufferWord3 = 0x00020000;
+
+template <int DT>
+struct Elem {
+  static constexpr int kBytes = (DT == PKV_F32) ? 4 : 2;
+};
+
+template <int DT, int D, int BS>
+struct Geo {
+  static constexpr int kBytes = Elem<DT>::kBytes;
+  static constexpr int kEpl = 16 / kBytes;       // elements per lane per 16-byte load
+  static constexpr int kLpr = D / kEpl;          // lanes per token row
+  static constexpr int kRpl = 64 / kLpr;         // token rows per wave-wide load
+  static constexpr int kLoads = BS / kRpl;       // wave-wide loads per K (or V) tile
+  static constexpr int kRowBytes = D * kBytes;
+  static constexpr int kTileBytes = BS * kRowBytes;
+  static constexpr int kStates = kWaves * kRpl;  // softmax states merged per work-group
+  static_assert(kLpr >= 8 && kLpr <= 32 && 64 % kLpr == 0, "row must span 8..32 lanes");
+  static_assert(BS % kRpl == 0, "block must hold whole wave-wide loads");
+};
+
+// ---- cross-lane sums (DPP within a 16-lane row; ds_swizzle-free) ----------
+constexpr int kDppQuad1032 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuad2301 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140;   // lane i <- lane 15 - i
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7 - i, within each 8
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the LPR lanes of a token row; every lane of the row gets the same
+// bits (each step adds a value and its partner's, in either order).
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp<kDppQuad1032>(x);
+  x += dpp<kDppQuad2301>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  if constexpr (LPR >= 16) x += dpp<kDppRowMirror>(x);
+  if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+// ---- element helpers --------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ T bits_as(unsigned int u) {
+  return __builtin_bit_cast(T, u);
+}
+
+// Partial dot product of the lane's 16-byte q column with a 16-byte K piece.
+template <int DT>
+__device__ __forceinline__ float dot16(const u32x4& q, const u32x4& k) {
+  if constexpr (DT == PKV_BF16) {
+    float a = __builtin_amdgcn_fdot2_f32_bf16(bits_as<bf16x2>(q.x), bits_as<bf16x2>(k.x), 0.f, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(bits_as<bf16x2>(q.y), bits_as<bf16x2>(k.y), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(bits_as<bf16x2>(q.z), bits_as<bf16x2>(k.z), a, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(bits_as<bf16x2>(q.w), bits_as<bf16x2>(k.w), a, false);
+  } else if constexpr (DT == PKV_F16) {
+    float a = __builtin_amdgcn_fdot2(bits_as<f16x2>(q.x), bits_as<f16x2>(k.x), 0.f, false);
+    a = __builtin_amdgcn_fdot2(bits_as<f16x2>(q.y), bits_as<f16x2>(k.y), a, false);
+    a = __builtin_amdgcn_fdot2(bits_as<f16x2>(q.z), bits_as<f16x2>(k.z), a, false);
+    return __builtin_amdgcn_fdot2(bits_as<f16x2>(q.w), bits_as<f16x2>(k.w), a, false);
+  } else {
+    float a = __uint_as_float(q.x) * __uint_as_float(k.x);
+    a = __builtin_fmaf(__uint_as_float(q.y), __uint_as_float(k.y), a);
+    a = __builtin_fmaf(__uint_as_float(q.z), __uint_as_float(k.z), a);
+    return __builtin_fmaf(__uint_as_float(q.w), __uint_as_float(k.w), a);
+  }
+}
+
+// acc[0 .. 16/elem) += p * (16-byte V piece)
+template <int DT>
+__device__ __forceinline__ void axpy16(float p, const u32x4& v, float* acc) {
+  const unsigned int w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (DT == PKV_BF16) {
+      acc[2 * i] = __builtin_fmaf(p, __uint_as_float(w[i] << 16), acc[2 * i]);
+      acc[2 * i + 1] = __builtin_fmaf(p, __uint_as_float(w[i] & 0xFFFF0000u), acc[2 * i + 1]);
+    } else if constexpr (DT == PKV_F16) {
+      const f16x2 h = bits_as<f16x2>(w[i]);
+      acc[2 * i] = __builtin_fmaf(p, float(h.x), acc[2 * i]);
+      acc[2 * i + 1] = __builtin_fmaf(p, float(h.y), acc[2 * i + 1]);
+    } else {
+      acc[i] = __builtin_fmaf(p, __uint_as_float(w[i]), acc[i]);
+    }
+  }
+}
+
+__device__ __forceinline__ unsigned short f32_to_bf16_rne(float x) {
+  unsigned int u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;   // NaN stays a quiet NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<unsigned short>(u >> 16);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_elem(void* base, int64_t i, float x) {
+  if constexpr (DT == PKV_F32) {
+    static_cast<float*>(base)[i] = x;
+  } else if constexpr (DT == PKV_F16) {
+    static_cast<unsigned short*>(base)[i] = __half_as_ushort(__float2half(x));
+  } else {
+    static_cast<unsigned short*>(base)[i] = f32_to_bf16_rne(x);
+  }
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Blocks [j0, j1) of partition p and the sequence's partition count.
+struct Span {
+  int nb, parts, j0, j1;
+};
+
+__device__ __forceinline__ bool context_ok(int32_t L, int32_t cap) { return L >= 0 && L <= cap; }
+
+template <int DT, int D, int BS>
+__global__ __launch_bounds__(kThreads) void decode_partition_kernel(
+    const void* __restrict__ q, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    void* __restrict__ out, float* __restrict__ ws_m, float* __restrict__ ws_l,
+    float* __restrict__ ws_acc, int64_t num_blocks, int32_t max_blocks, int32_t part_blocks,
+    int32_t partitions, float scale_log2) {
+  using G = Geo<DT, D, BS>;
+  const int h = blockIdx.x;
+  const int p = blockIdx.y;
+  const int s = blockIdx.z;
+  const int H = gridDim.x;
+  const int64_t row = int64_t(s) * H + h;                 // (sequence, head) row of q / out
+  const int32_t L = context_lens[s];
+
+  if (L == 0 || !context_ok(L, max_blocks * BS)) {       // empty row, or a broken contract
+    if (p == 0 && threadIdx.x < D) store_elem<DT>(out, row * D + threadIdx.x, L == 0 ? 0.f : __builtin_nanf(""));
+    return;
+  }
+  const int nb = (L + BS - 1) / BS;
+  const int parts = (nb + part_blocks - 1) / part_blocks;
+  if (p >= parts) return;
+  const int j0 = p * part_blocks;
+  const int j1 = min(j0 + part_blocks, nb);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane / G::kLpr;                           // token row within a wave-wide load
+  const int c = lane % G::kLpr;                           // 16-byte column within the row
+
+  const u32x4 qv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(q) +
+                                                   (row * D + c * G::kEpl) * G::kBytes);
+
+  // This wave's blocks: i-th is logical block j0 + wave + kWaves * i.
+  const int span = j1 - j0;
+  const int n_my = span > wave ? (span - wave + kWaves - 1) / kWaves : 0;
+  const int32_t* trow = block_tables + int64_t(s) * max_blocks + j0 + wave;
+
+  float m = kEmptyMax, l = 0.f;
+  float acc[G::kEpl];
+#pragma unroll
+  for (int e = 0; e < G::kEpl; ++e) acc[e] = 0.f;
+  bool bad = false;
+
+  auto table_at = [&](int i) -> int32_t {
+    const int ic = i < n_my ? i : n_my - 1;
+    return __builtin_amdgcn_readfirstlane(trow[kWaves * ic]);
+  };
+
+  // Issue the loads of this wave's i-th block into (kb, vb).  Past the wave's
+  // last block the resource is empty: the loads return zeros, touch nothing.
+  auto issue = [&](u32x4* kb, u32x4* vb, int i, int32_t bid) {
+    const bool live = i < n_my;
+    const int j = j0 + wave + kWaves * i;
+    const int ntok = min(L - j * BS, BS);
+    const bool id_ok = static_cast<uint64_t>(static_cast<int64_t>(bid)) < static_cast<uint64_t>(num_blocks);
+    bad = bad || (live && !id_ok);
+    const int nrec = (live && id_ok) ? ntok * G::kRowBytes : 0;
+    const int64_t tile = (int64_t(id_ok ? bid : 0) * H + h) * G::kTileBytes;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(k_cache + tile), 0, nrec, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(v_cache + tile), 0, nrec, kBufferWord3);
+#pragma unroll
+    for (int t = 0; t < G::kLoads; ++t)
+      kb[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (t * 64 + lane) * 16, 0, 0));
+#pragma unroll
+    for (int t = 0; t < G::kLoads; ++t)
+      vb[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (t * 64 + lane) * 16, 0, 0));
+  };
+
+  // Fold this wave's i-th block into the row's running softmax state.
+  auto consume = [&](const u32x4* kb, const u32x4* vb, int i) {
+    const int j = j0 + wave + kWaves * i;
+    const int ntok = i < n_my ? L - j * BS : 0;           // rows at or past it are masked
+    float sc[G::kLoads];
+    float bm = kEmptyMax;
+#pragma unroll
+    for (int t = 0; t < G::kLoads; ++t) {
+      const float d = row_sum<G::kLpr>(dot16<DT>(qv, kb[t])) * scale_log2;
+      sc[t] = (t * G::kRpl + r < ntok) ? d : -__builtin_inff();
+      bm = fmaxf(bm, sc[t]);
+    }
+    const float m_new = fmaxf(m, bm);
+    const float alpha = exp2_fast(m - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < G::kEpl; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int t = 0; t < G::kLoads; ++t) {
+      const float pr = exp2_fast(sc[t] - m_new);
+      l += pr;
+      axpy16<DT>(pr, vb[t], acc);
+    }
+    m = m_new;
+  };
+
+  // Two-deep pipeline over buffers A and B: block i+1's loads are issued
+  // before block i is consumed.  The body has no branch between a buffer's
+  // loads and its consumer (a trailing odd step consumes an empty buffer,
+  // which leaves the state bit-for-bit unchanged), so the compiler cannot sink
+  // the loads below the consumer; the scheduling barriers keep the machine
+  // scheduler from doing the same inside the block.
+  if (n_my > 0) {
+    u32x4 kA[G::kLoads], vA[G::kLoads], kB[G::kLoads], vB[G::kLoads];
+    int32_t t_next = table_at(1);
+    issue(kA, vA, 0, table_at(0));
+    for (int i = 0; i < n_my; i += 2) {
+      const int32_t t2 = table_at(i + 2);
+      issue(kB, vB, i + 1, t_next);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(kA, vA, i);
+      __builtin_amdgcn_sched_barrier(0);
+      t_next = table_at(i + 3);
+      issue(kA, vA, i + 2, t2);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(kB, vB, i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Merge the kStates row states of the work-group.
+  __shared__ float sm_m[G::kStates];
+  __shared__ float sm_l[G::kStates];
+  __shared__ float sm_acc[G::kStates * D];
+  __shared__ int sm_bad[kWaves];
+  const int st = wave * G::kRpl + r;
+  if (c == 0) {
+    sm_m[st] = m;
+    sm_l[st] = l;
+  }
+  if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
+#pragma unroll
+  for (int e = 0; e < G::kEpl; ++e) sm_acc[st * D + c * G::kEpl + e] = acc[e];
+  __syncthreads();
+
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    float M = kEmptyMax;
+#pragma unroll
+    for (int k = 0; k < G::kStates; ++k) M = fmaxf(M, sm_m[k]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int k = 0; k < G::kStates; ++k) {
+      const float w = exp2_fast(sm_m[k] - M);
+      num = __builtin_fmaf(w, sm_acc[k * D + d], num);
+      den = __builtin_fmaf(w, sm_l[k], den);
+    }
+    int any_bad = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) any_bad |= sm_bad[w];
+    if (any_bad) den = __builtin_nanf("");
+    if (parts == 1) {
+      store_elem<DT>(out, row * D + d, num / den);
+    } else {
+      const int64_t wi = row * partitions + p;
+      ws_acc[wi * D + d] = num;
+      if (d == 0) {
+        ws_m[wi] = M;
+        ws_l[wi] = den;
+      }
+    }
+  }
+}
+
+// Merge the partitions of every (sequence, head) whose context spans more
+// than one: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+template <int DT, int D>
+__global__ __launch_bounds__(D) void lse_reduce_kernel(
+    const int32_t* __restrict__ context_lens, const float* __restrict__ ws_m,
+    const float* __restrict__ ws_l, const float* __restrict__ ws_acc, void* __restrict__ out,
+    int32_t max_blocks, int32_t block_size, int32_t part_blocks, int32_t partitions) {
+  const int h = blockIdx.x;
+  const int s = blockIdx.y;
+  const int H = gridDim.x;
+  const int d = threadIdx.x;
+  const int32_t L = context_lens[s];
+  if (L <= 0 || !context_ok(L, max_blocks * block_size)) return;
+  const int nb = (L + block_size - 1) / block_size;
+  const int parts = (nb + part_blocks - 1) / part_blocks;
+  if (parts <= 1) return;
+  const int64_t row = int64_t(s) * H + h;
+  const int64_t base = row * partitions;
+  float M = kEmptyMax;
+  for (int p = 0; p < parts; ++p) M = fmaxf(M, ws_m[base + p]);
+  float num = 0.f, den = 0.f;
+  for (int p = 0; p < parts; ++p) {
+    const float w = exp2_fast(ws_m[base + p] - M);
+    num = __builtin_fmaf(w, ws_acc[(base + p) * D + d], num);
+    den = __builtin_fmaf(w, ws_l[base + p], den);
+  }
+  store_elem<DT>(out, row * D + d, num / den);
+}
+
+template <int DT, int D, int BS>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(unsigned(a.num_heads), unsigned(a.partitions), unsigned(a.num_seqs));
+  hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS>), grid, dim3(kThreads), 0, stream, a.q,
+                     static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
+                     a.block_tables, a.context_lens, a.out, a.ws_m, a.ws_l, a.ws_acc, a.num_blocks,
+                     a.max_blocks, a.part_blocks, a.partitions, a.scale_log2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.partitions <= 1) return e;
+  hipLaunchKernelGGL((lse_reduce_kernel<DT, D>), dim3(unsigned(a.num_heads), unsigned(a.num_seqs)),
+                     dim3(D), 0, stream, a.context_lens, a.ws_m, a.ws_l, a.ws_acc, a.out,
+                     a.max_blocks, BS, a.part_blocks, a.partitions);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(int head_dim, int block_size, const DecodeArgs& a, hipStream_t stream) {
+  if (head_dim == 64) {
+    return block_size == 16 ? launch_typed<DT, 64, 16>(a, stream) : launch_typed<DT, 64, 32>(a, stream);
+  }
+  return block_size == 16 ? launch_typed<DT, 128, 16>(a, stream) : launch_typed<DT, 128, 32>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodeArgs& a,
+                         hipStream_t stream) {
+  switch (dtype) {
+    case PKV_F32: return launch_dt<PKV_F32>(head_dim, block_size, a, stream);
+    case PKV_F16: return launch_dt<PKV_F16>(head_dim, block_size, a, stream);
+    default: return launch_dt<PKV_BF16>(head_dim, block_size, a, stream);
+  }
+}
+
+}  // namespace pkv

@@ -95,6 +95,14 @@ class Case:
             self.k_pool = np.full((NB, H, bs, D), fill, dtype=np.uint16)
             self.v_pool = np.full((NB, H, bs, D), fill, dtype=np.uint16)
             to_py = bf16_value
+        elif dtype == "f16":
+            self.q = rng.standard_normal((B, H, D)).astype(np.float16)
+            self.Klog = [rng.standard_normal((L, H, D)).astype(np.float16) for L in lens]
+            self.Vlog = [rng.standard_normal((L, H, D)).astype(np.float16) for L in lens]
+            fill = np.float16(np.nan) if poison else np.float16(0)
+            self.k_pool = np.full((NB, H, bs, D), fill, dtype=np.float16)
+            self.v_pool = np.full((NB, H, bs, D), fill, dtype=np.float16)
+            to_py = float
         else:
             raise ValueError(dtype)
         self.to_py = to_py
