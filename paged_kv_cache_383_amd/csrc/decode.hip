@@ -11,10 +11,11 @@
 // independently and merged by log-sum-exp weights (the card names this
 // FlashDecoding in "헷갈리기 쉬운 구분").
 //
-// Work decomposition.  One work-group of 4 wave64s per (head, partition,
-// sequence); the grid's fastest index is the head, so work-groups running
-// together read neighbouring (block, head) tiles of the same physical blocks.
-// Wave w of a partition takes its blocks w, w+4, w+8, ...
+// Work decomposition.  One work-group of W wave64s (W = 8 for 16-token
+// blocks, 4 for 32-token blocks) per (head, partition, sequence); the grid's
+// fastest index is the head, so work-groups running together read
+// neighbouring (block, head) tiles of the same physical blocks.  Wave w of a
+// partition takes its blocks w, w+W, w+2W, ...
 //
 // Data movement.  A (block, head) tile of K is block_size * head_dim elements
 // in one contiguous run ("vLLM의 PagedAttention 아키텍처와 GPU 메모리 최적화 원리",
@@ -31,7 +32,7 @@
 // Arithmetic.  q.k uses the packed dot2 instructions for 16-bit types (exact
 // products, fp32 sums) and fp32 FMA for fp32; each row's partial dots are
 // summed across its 8/16/32 lanes with DPP.  The 16 lanes of a row then hold
-// identical scores, so every token row of a wave (4 per load) keeps its own
+// identical scores, so every token row of a wave (4 per 1 KiB load) keeps its own
 // running (max, sum, acc) state in registers with no cross-row traffic in the
 // loop; rows and waves are merged once at the end through LDS.  Scores are
 // base-2 logits (scale * log2 e folded in) so exp is a single v_exp_f32.
@@ -47,8 +48,23 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+// Cache policy of the K/V tile loads (the buffer-load aux operand).  Every
+// tile is read exactly once per call, so the loads are marked non-temporal
+// (nt = bit 1 on gfx950): on MI355X this streams the cache through L2 and
+// Infinity Cache without displacing reusable lines, and measured 10-12 %
+// faster than the default policy on every configuration.
+#ifndef PKV_KV_LOAD_POLICY
+#define PKV_KV_LOAD_POLICY 2
+#endif
+constexpr int kLoadPolicy = PKV_KV_LOAD_POLICY;
+
+// Waves per work-group: 8 for 16-token blocks (shorter work-groups, smaller
+// tail at the end of the grid), 4 for 32-token blocks (twice the registers
+// per wave for the larger tiles).
+template <int BS>
+constexpr int waves_for() {
+  return BS == 16 ? 8 : 4;
+}
 // Running max before any token is seen.  Finite, so 2^(m - m') is defined
 // while a row has seen only masked tokens; any real score exceeds it.
 constexpr float kEmptyMax = -3.0e38f;
@@ -60,7 +76,7 @@ struct Elem {
   static constexpr int kBytes = (DT == PKV_F32) ? 4 : 2;
 };
 
-template <int DT, int D, int BS>
+template <int DT, int D, int BS, int WAVES>
 struct Geo {
   static constexpr int kBytes = Elem<DT>::kBytes;
   static constexpr int kEpl = 16 / kBytes;       // elements per lane per 16-byte load
@@ -69,7 +85,9 @@ struct Geo {
   static constexpr int kLoads = BS / kRpl;       // wave-wide loads per K (or V) tile
   static constexpr int kRowBytes = D * kBytes;
   static constexpr int kTileBytes = BS * kRowBytes;
-  static constexpr int kStates = kWaves * kRpl;  // softmax states merged per work-group
+  static constexpr int kWaves = WAVES;
+  static constexpr int kThreads = 64 * WAVES;
+  static constexpr int kStates = WAVES * kRpl;    // softmax states merged per work-group
   static_assert(kLpr >= 8 && kLpr <= 32 && 64 % kLpr == 0, "row must span 8..32 lanes");
   static_assert(BS % kRpl == 0, "block must hold whole wave-wide loads");
 };
@@ -163,21 +181,17 @@ __device__ __forceinline__ void store_elem(void* base, int64_t i, float x) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Blocks [j0, j1) of partition p and the sequence's partition count.
-struct Span {
-  int nb, parts, j0, j1;
-};
-
 __device__ __forceinline__ bool context_ok(int32_t L, int32_t cap) { return L >= 0 && L <= cap; }
 
-template <int DT, int D, int BS>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(
+template <int DT, int D, int BS, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
     const void* __restrict__ q, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     void* __restrict__ out, float* __restrict__ ws_m, float* __restrict__ ws_l,
     float* __restrict__ ws_acc, int64_t num_blocks, int32_t max_blocks, int32_t part_blocks,
     int32_t partitions, float scale_log2) {
-  using G = Geo<DT, D, BS>;
+  using G = Geo<DT, D, BS, WAVES>;
+  constexpr int kWaves = WAVES;
   const int h = blockIdx.x;
   const int p = blockIdx.y;
   const int s = blockIdx.z;
@@ -235,10 +249,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(v_cache + tile), 0, nrec, kBufferWord3);
 #pragma unroll
     for (int t = 0; t < G::kLoads; ++t)
-      kb[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (t * 64 + lane) * 16, 0, 0));
+      kb[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (t * 64 + lane) * 16, 0, kLoadPolicy));
 #pragma unroll
     for (int t = 0; t < G::kLoads; ++t)
-      vb[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (t * 64 + lane) * 16, 0, 0));
+      vb[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (t * 64 + lane) * 16, 0, kLoadPolicy));
   };
 
   // Fold this wave's i-th block into the row's running softmax state.
@@ -367,7 +381,8 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(
 template <int DT, int D, int BS>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(unsigned(a.num_heads), unsigned(a.partitions), unsigned(a.num_seqs));
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS>), grid, dim3(kThreads), 0, stream, a.q,
+  constexpr int kWaves = waves_for<BS>();
+  hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, kWaves>), grid, dim3(64 * kWaves), 0, stream, a.q,
                      static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
                      a.block_tables, a.context_lens, a.out, a.ws_m, a.ws_l, a.ws_acc, a.num_blocks,
                      a.max_blocks, a.part_blocks, a.partitions, a.scale_log2);
