@@ -99,6 +99,52 @@ def cpu_baseline(meta, w, budget_s=10.0):
             "tokens_heads_per_s": round(tokens / wall, 1)}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partition_llama13b_b64_hbm_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_383_amd", "csrc", f) for f in ("decode.hip", "pkv_internal.h")]
+
+
+def kernel_fingerprint():
+    """sha256 over the decode kernel's sources and compile flags: counters taken on another
+    version of the kernel no longer describe this one."""
+    import hashlib
+    from paged_kv_cache_383_amd import build as b
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    h.update(" ".join(b.compile_flags()).replace(ROOT, "").encode())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, partition):
+    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or
+    None when that summary was taken on a different kernel, workload or partition size."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if line.startswith("traffic-json:"):
+                t = json.loads(line.split(":", 1)[1])
+                if (t.get("kernel_sha256") == kernel_fingerprint() and t.get("workload") == workload
+                        and t.get("partition_size") == partition):
+                    return t
+    return None
+
+
+def copy_calibration(mib):
+    """A plain elementwise copy of known size (read N bytes, write N bytes) whose FETCH_SIZE / WRITE_SIZE
+    counters calibrate the decode kernel's: run under rocprofv3 --pmc beside the bench."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": "torch.neg fp32", "bytes_read": n * 4, "bytes_written": n * 4,
+                      "launches": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,11 +154,16 @@ def main():
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--rotate", type=int, default=None, help="independent input copies cycled over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=None, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the decode path has no multi-GPU variant in this library "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import numpy as np
     import torch
@@ -175,6 +226,7 @@ def main():
         cpu = cpu_baseline(meta, sets[0])
         log(f"cpu oracle: {cpu}")
 
+    traffic = measured_traffic(cfg.name, part)
     th = meta.total_tokens * cfg.num_heads
     rec = {
         "metric": METRIC,
@@ -211,7 +263,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else traffic["bytes_per_launch"],
             "algorithmic_bytes_per_launch": nbytes["decode"],
             "mean_launch_us": round(decode_us, 2),
         },
