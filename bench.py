@@ -12,10 +12,13 @@ in the caches.
 
 Prints one JSON line:
   value          algorithmic GB/s of the whole step (write + decode bytes / step time)
-  roofline       the decode call (partition kernel + LSE reduce), algorithmic bytes per
-                 launch / its mean duration from HIP events on the launch stream, vs the
-                 8 TB/s HBM peak
+  roofline       the decode call (the partition kernel, plus the LSE reduce when the
+                 context is split), algorithmic bytes per launch / its mean duration from
+                 HIP events on the launch stream, vs the 8 TB/s HBM peak
   cpu_baseline   the float64 CPU oracle on a bounded sample of the same workload
+Timing: the K steps run back to back with no event between them (wall clock and one HIP event
+pair bracket them); then the decode call alone and the write alone run K times back to back, each
+bracketed by a HIP event pair, for the per-launch averages.
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--config 2]
 """
 from __future__ import annotations
@@ -151,7 +154,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="split-context partition in tokens (0 = one pass); default: the library's choice")
     ap.add_argument("--rotate", type=int, default=None, help="independent input copies cycled over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=None, metavar="MIB",
@@ -178,47 +182,70 @@ def main():
     dev = torch.device("cuda:0")
     meta = W.make_metadata(args.config)
     cfg = meta.cfg
-    part = cfg.partition_size if args.partition_size is None else args.partition_size
+    part = pkv.PARTITION_AUTO if args.partition_size is None else args.partition_size
+    resolved = pkv.paged_attention_partition_size(len(meta.context_lens), cfg.num_heads, cfg.max_blocks,
+                                                  cfg.block_size, part)
     nbytes = algorithmic_bytes(meta)
     per_set = 2 * meta.num_blocks * cfg.num_heads * cfg.block_size * cfg.head_dim * elem_bytes(cfg.dtype)
     rotate = args.rotate or max(2, math.ceil(1.0e9 / per_set))
     log(f"config {cfg.cfg_id} {cfg.name}: B={len(meta.context_lens)} sum(L)={meta.total_tokens} "
-        f"pool={meta.num_blocks} blocks ({per_set / 1e9:.2f} GB K+V), {rotate} rotating input sets, partition {part}")
+        f"pool={meta.num_blocks} blocks ({per_set / 1e9:.2f} GB K+V), {rotate} rotating input sets, "
+        f"partition {part} -> {resolved} tokens")
     sets = [W.make_workload(meta, dev, seed=meta.seed + 1000 * r) for r in range(rotate)]
     outs = [torch.empty_like(s.q) for s in sets]
     wsb = pkv.paged_attention_workspace_bytes(len(meta.context_lens), cfg.num_heads, cfg.head_dim,
                                               cfg.max_blocks, cfg.block_size, part)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
-    def step(i, ev=None):
+    def write(i):
         s = sets[i % rotate]
-        if ev is not None:
-            ev[0].record()
         pkv.paged_kv_write(s.k_new, s.v_new, s.slot_mapping, s.k_cache, s.v_cache)
-        if ev is not None:
-            ev[1].record()
+
+    def decode(i):
+        s = sets[i % rotate]
         pkv.paged_attention_decode(s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens, cfg.scale,
                                    out=outs[i % rotate], workspace=ws, partition_size=part)
-        if ev is not None:
-            ev[2].record()
 
     for i in range(args.warmup):
-        step(i)
+        write(i)
+        decode(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    # Timed region 1: whole steps (write + decode), no per-step events (an event record between
+    # kernels adds several microseconds of queue work); wall clock and a HIP event pair around it.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
     for i in range(args.steps):
-        step(i, evs[i])
+        write(i)
+        decode(i)
+    ev1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
-    write_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
-    decode_us = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
-    decode_med_us = float(np.median([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+    step_ev_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+
+    # Timed region 2: the dominant kernel alone, launched back to back over the rotating inputs on the
+    # stream the library launches on (torch's current stream); average launch duration from a HIP
+    # event pair, the same quantity a rocprofv3 kernel trace averages.
+    ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev2.record()
+    for i in range(args.steps):
+        decode(i)
+    ev3.record()
+    torch.cuda.synchronize()
+    decode_us = ev2.elapsed_time(ev3) * 1e3 / args.steps
+    # Timed region 3: the write alone, likewise.
+    ev2.record()
+    for i in range(args.steps):
+        write(i)
+    ev3.record()
+    torch.cuda.synchronize()
+    write_us = ev2.elapsed_time(ev3) * 1e3 / args.steps
     achieved = nbytes["decode"] / (decode_us * 1e-6) / 1e9
-    log(f"step {step_s * 1e6:.1f} us (wall), write {write_us:.1f} us, decode {decode_us:.1f} us "
-        f"(median {decode_med_us:.1f}) -> decode {achieved:.0f} GB/s = {achieved / PEAK_HBM_GBS:.1%} of peak")
+    log(f"step {step_s * 1e6:.1f} us (wall; {step_ev_us:.1f} us by events), decode {decode_us:.1f} us, "
+        f"write {write_us:.1f} us -> decode {achieved:.0f} GB/s = {achieved / PEAK_HBM_GBS:.1%} of peak")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -226,7 +253,7 @@ def main():
         cpu = cpu_baseline(meta, sets[0])
         log(f"cpu oracle: {cpu}")
 
-    traffic = measured_traffic(cfg.name, part)
+    traffic = measured_traffic(cfg.name, resolved)
     th = meta.total_tokens * cfg.num_heads
     rec = {
         "metric": METRIC,
@@ -249,15 +276,17 @@ def main():
             "block_size": cfg.block_size,
             "sum_context_tokens": meta.total_tokens,
             "pool_blocks": meta.num_blocks,
-            "partition_size": part,
+            "partition_size": resolved,
+            "partition_choice": "library (PKV_PARTITION_AUTO)" if part == pkv.PARTITION_AUTO else "caller",
             "step": "paged_kv_write(one new token per sequence) + paged_attention_decode",
             "step_algorithmic_bytes": nbytes["step"],
         },
         "tokens_heads_per_s": round(th / step_s, 1),
         "fraction_of_peak": round(nbytes["step"] / step_s / 1e9 / PEAK_HBM_GBS, 4),
-        "kernels_us": {"paged_kv_write": round(write_us, 2), "paged_attention_decode": round(decode_us, 2)},
+        "kernels_us": {"paged_kv_write": round(write_us, 2), "paged_attention_decode": round(decode_us, 2),
+                       "step_by_events": round(step_ev_us, 2)},
         "roofline": {
-            "kernel": "paged_attention_decode (decode_partition_kernel + lse_reduce_kernel)",
+            "kernel": "paged_attention_decode (decode_partition_kernel" + (" + lse_reduce_kernel)" if resolved else ")"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,

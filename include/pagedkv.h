@@ -63,6 +63,9 @@ extern "C" {
 
 typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
 
+/* partition_size value that lets the library choose the split (see below). */
+#define PKV_PARTITION_AUTO (-1)
+
 typedef enum {
   PKV_OK = 0,
   PKV_EINVAL = 1,        /* bad argument: null pointer, negative or inconsistent size      */
@@ -95,6 +98,19 @@ int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping, in
                    int32_t head_dim, int32_t block_size, int32_t dtype, void* stream);
 
 /*
+ * paged_attention_partition_size -- the partition size, in tokens, that
+ * paged_attention_decode uses for these sizes: partition_size itself, or for
+ * PKV_PARTITION_AUTO the library's choice.  The automatic choice is 0 (no
+ * split) when num_seqs * num_heads >= 1024, since the grid then already holds
+ * several work-groups per compute unit; otherwise the smallest multiple of 512
+ * tokens that cuts the table's capacity (max_blocks_per_seq * block_size) into
+ * about 4096 / (num_seqs * num_heads) partitions, or 0 if that is the whole
+ * capacity.  Results do not depend on the split beyond fp32 rounding.
+ */
+int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                       int32_t block_size, int32_t partition_size);
+
+/*
  * paged_attention_workspace_bytes -- device scratch that paged_attention_decode
  * needs for its split-context partials with these sizes (0 when no sequence
  * can span more than one partition).  Returns 0 for invalid sizes as well;
@@ -118,7 +134,8 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
  * Long contexts are split into partitions of partition_size tokens, each
  * reduced independently and then merged by log-sum-exp weights; the result is
  * the same softmax (the pages name this FlashDecoding, [card] "헷갈리기 쉬운 구분").
- * partition_size must be a multiple of block_size; 0 means never split.
+ * partition_size must be a multiple of block_size; 0 means never split and
+ * PKV_PARTITION_AUTO lets the library choose (paged_attention_partition_size).
  *
  *   q             [num_seqs, num_heads, head_dim], dtype, read
  *   k_cache,

@@ -8,9 +8,14 @@ If the library is not built, every call raises.
 
     paged_kv_write(k, v, slot_mapping, k_cache, v_cache)
     paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale,
-                           out=None, workspace=None, partition_size=512)
+                           out=None, workspace=None, partition_size=PARTITION_AUTO)
     paged_attention_workspace_bytes(num_seqs, num_heads, head_dim,
                                     max_blocks_per_seq, block_size, partition_size)
+    paged_attention_partition_size(num_seqs, num_heads, max_blocks_per_seq, block_size,
+                                   partition_size)
+
+partition_size: tokens per split-context partition, 0 for one pass per
+sequence, or PARTITION_AUTO (the default) to let the library choose.
 """
 from __future__ import annotations
 
@@ -20,7 +25,8 @@ import os
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
 PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = 0, 1, 2, 3, 4
 STATUS_NAMES = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP"}
-DEFAULT_PARTITION = 512
+PARTITION_AUTO = -1            # let the library choose the split-context partition
+DEFAULT_PARTITION = PARTITION_AUTO
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpagedkv.so")
 _lib = None
@@ -43,6 +49,8 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         L.paged_kv_write.argtypes = [vp, vp, vp, i64, vp, vp, i64, i32, i32, i32, i32, vp]
         L.paged_kv_write.restype = ctypes.c_int
+        L.paged_attention_partition_size.argtypes = [i32, i32, i32, i32, i32]
+        L.paged_attention_partition_size.restype = i32
         L.paged_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
         L.paged_attention_workspace_bytes.restype = sz
         L.paged_attention_decode.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i64,
@@ -102,6 +110,13 @@ def paged_kv_write(k, v, slot_mapping, k_cache, v_cache):
         _check(lib().paged_kv_write(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k.shape[0],
                                     k_cache.data_ptr(), v_cache.data_ptr(), NB, H, D, bs,
                                     _dtype_code(k_cache), _stream(k_cache.device)))
+
+
+def paged_attention_partition_size(num_seqs, num_heads, max_blocks_per_seq, block_size,
+                                   partition_size=DEFAULT_PARTITION) -> int:
+    """The partition size (tokens; 0 = no split) the decode call uses for these sizes."""
+    return int(lib().paged_attention_partition_size(num_seqs, num_heads, max_blocks_per_seq, block_size,
+                                                    partition_size))
 
 
 def paged_attention_workspace_bytes(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size,

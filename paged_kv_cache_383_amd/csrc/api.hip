@@ -69,16 +69,44 @@ int32_t part_blocks_for(int32_t max_blocks, int32_t block_size, int32_t partitio
   return partition_size == 0 ? max_blocks : partition_size / block_size;
 }
 
+// Automatic split.  With at least kAutoMinRows (sequence, head) rows the grid
+// already holds several work-groups per compute unit, and one pass per row
+// is fastest (no partials, no merge).  With fewer rows, contexts are cut into
+// partitions, multiples of kAutoGrain tokens, so that about
+// kAutoTargetGroups work-groups cover the longest possible context.
+constexpr int64_t kAutoMinRows = 1024;
+constexpr int64_t kAutoTargetGroups = 4096;
+constexpr int64_t kAutoGrain = 512;
+
+int32_t resolve_partition(int32_t num_seqs, int32_t num_heads, int32_t max_blocks, int32_t block_size,
+                          int32_t partition_size) {
+  if (partition_size != PKV_PARTITION_AUTO) return partition_size;
+  const int64_t rows = int64_t(num_seqs) * num_heads;
+  const int64_t cap = int64_t(max_blocks) * block_size;
+  if (rows <= 0 || rows >= kAutoMinRows) return 0;
+  const int64_t want = (kAutoTargetGroups + rows - 1) / rows;
+  int64_t part = (cap + want - 1) / want;
+  part = (part + kAutoGrain - 1) / kAutoGrain * kAutoGrain;
+  return part >= cap ? 0 : int32_t(part);
+}
+
 }  // namespace
 
 extern "C" const char* pkv_last_error(void) { return g_last_error.c_str(); }
 
+extern "C" int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_heads,
+                                                  int32_t max_blocks_per_seq, int32_t block_size,
+                                                  int32_t partition_size) {
+  return resolve_partition(num_seqs, num_heads, max_blocks_per_seq, block_size, partition_size);
+}
+
 extern "C" size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                                   int32_t head_dim, int32_t max_blocks_per_seq,
                                                   int32_t block_size, int32_t partition_size) {
-  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
-      block_size <= 0 || partition_size < 0 || partition_size % block_size != 0)
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 || block_size <= 0)
     return 0;
+  partition_size = resolve_partition(num_seqs, num_heads, max_blocks_per_seq, block_size, partition_size);
+  if (partition_size < 0 || partition_size % block_size != 0) return 0;
   const int32_t pb = part_blocks_for(max_blocks_per_seq, block_size, partition_size);
   return pkv::workspace_layout(num_seqs, num_heads, head_dim, partitions_for(max_blocks_per_seq, pb)).bytes;
 }
@@ -129,9 +157,10 @@ extern "C" int paged_attention_decode(const void* q, const void* k_cache, const 
     return fail(PKV_EINVAL, "max_blocks_per_seq must be positive (got %d)", max_blocks_per_seq);
   if (int64_t(max_blocks_per_seq) * block_size > INT32_MAX)
     return fail(PKV_EUNSUPPORTED, "table capacity of %lld tokens exceeds int32", (long long)max_blocks_per_seq * block_size);
-  if (partition_size < 0 || partition_size % block_size != 0)
-    return fail(PKV_EINVAL, "partition_size %d must be 0 or a positive multiple of block_size %d",
-                partition_size, block_size);
+  if (partition_size != PKV_PARTITION_AUTO && (partition_size < 0 || partition_size % block_size != 0))
+    return fail(PKV_EINVAL, "partition_size %d must be PKV_PARTITION_AUTO (-1), 0 or a positive multiple of "
+                "block_size %d", partition_size, block_size);
+  partition_size = resolve_partition(num_seqs, num_heads, max_blocks_per_seq, block_size, partition_size);
   if (!isfinite(scale)) return fail(PKV_EINVAL, "scale must be finite");
   if (num_seqs == 0) return ok();
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)

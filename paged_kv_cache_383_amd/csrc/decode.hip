@@ -14,8 +14,10 @@
 // Work decomposition.  One work-group of W wave64s (W = 8 for 16-token
 // blocks, 4 for 32-token blocks) per (head, partition, sequence); the grid's
 // fastest index is the head, so work-groups running together read
-// neighbouring (block, head) tiles of the same physical blocks.  Wave w of a
-// partition takes its blocks w, w+W, w+2W, ...
+// neighbouring (block, head) tiles of the same physical blocks.  A wave works
+// in stages of TPS consecutive blocks (one 32-token or two 16-token bf16/fp16
+// tiles: 8 KiB of K and 8 KiB of V); wave w of a partition takes stages w,
+// w+W, w+2W, ...
 //
 // Data movement.  A (block, head) tile of K is block_size * head_dim elements
 // in one contiguous run ("vLLM의 PagedAttention 아키텍처와 GPU 메모리 최적화 원리",
@@ -26,8 +28,8 @@
 // tiles go straight from HBM to VGPRs: there is no cross-lane reuse for an LDS
 // round trip to serve.  Loads use a buffer resource sized to the tile's valid
 // rows: rows past the context end (and the whole tile of an invalid block id)
-// read as zero without touching memory.  Two tile buffers per wave keep the
-// next block's K and V in flight while the current one is consumed.
+// read as zero without touching memory.  A ring of 2 or 3 stage buffers per
+// wave keeps the next stages' K and V loads in flight while one is consumed.
 //
 // Arithmetic.  q.k uses the packed dot2 instructions for 16-bit types (exact
 // products, fp32 sums) and fp32 FMA for fp32; each row's partial dots are
@@ -58,9 +60,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #endif
 constexpr int kLoadPolicy = PKV_KV_LOAD_POLICY;
 
-// Waves per work-group: 8 for 16-token blocks (shorter work-groups, smaller
-// tail at the end of the grid), 4 for 32-token blocks (twice the registers
-// per wave for the larger tiles).
+// Waves per work-group: 8 for 16-token blocks, 4 for 32-token blocks (twice
+// the registers per stage).
 template <int BS>
 constexpr int waves_for() {
   return BS == 16 ? 8 : 4;
@@ -75,6 +76,25 @@ template <int DT>
 struct Elem {
   static constexpr int kBytes = (DT == PKV_F32) ? 4 : 2;
 };
+
+// Blocks loaded per pipeline stage: enough (block, head) tiles for 8 KiB of K
+// (and 8 KiB of V) per wave, so a bf16 stage of 16-token blocks takes two
+// tiles and moves as much as one 32-token tile does.
+constexpr int kStageBytes = 8192;
+template <int DT, int D, int BS>
+constexpr int tiles_for() {
+  constexpr int tile = BS * D * Elem<DT>::kBytes;
+  return tile >= kStageBytes ? 1 : kStageBytes / tile;
+}
+// Pipeline depth: stages in flight per wave.  For 16-bit types, three
+// single-tile stages or two double-tile ones keep 16 KiB of loads outstanding
+// per wave within the register budget (measured: 3 beats 2 for 32-token fp16
+// tiles by 3 %; two double-tile stages beat three single ones for 16-token
+// bf16 tiles).  fp32 tiles are twice as large: two stages.
+template <int DT, int TPS>
+constexpr int stages_for() {
+  return (DT == PKV_F32 || TPS > 1) ? 2 : 3;
+}
 
 template <int DT, int D, int BS, int WAVES>
 struct Geo {
@@ -183,7 +203,7 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ bool context_ok(int32_t L, int32_t cap) { return L >= 0 && L <= cap; }
 
-template <int DT, int D, int BS, int WAVES>
+template <int DT, int D, int BS, int WAVES, int TPS, int NST>
 __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
     const void* __restrict__ q, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
@@ -217,10 +237,12 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
   const u32x4 qv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(q) +
                                                    (row * D + c * G::kEpl) * G::kBytes);
 
-  // This wave's blocks: i-th is logical block j0 + wave + kWaves * i.
+  // This wave's stages: stage i covers the TPS consecutive logical blocks
+  // j0 + (wave + kWaves * i) * TPS + u, u < TPS (blocks at or past j1 are empty).
   const int span = j1 - j0;
-  const int n_my = span > wave ? (span - wave + kWaves - 1) / kWaves : 0;
-  const int32_t* trow = block_tables + int64_t(s) * max_blocks + j0 + wave;
+  const int units = (span + TPS - 1) / TPS;
+  const int n_my = units > wave ? (units - wave + kWaves - 1) / kWaves : 0;
+  const int32_t* trow = block_tables + int64_t(s) * max_blocks;
 
   float m = kEmptyMax, l = 0.f;
   float acc[G::kEpl];
@@ -228,44 +250,59 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
   for (int e = 0; e < G::kEpl; ++e) acc[e] = 0.f;
   bool bad = false;
 
-  auto table_at = [&](int i) -> int32_t {
-    const int ic = i < n_my ? i : n_my - 1;
-    return __builtin_amdgcn_readfirstlane(trow[kWaves * ic]);
+  auto first_block = [&](int i) { return j0 + (wave + kWaves * i) * TPS; };
+  // Physical ids of stage i's blocks (entries past the span are not read).
+  auto table_at = [&](int i, int32_t* ids) {
+#pragma unroll
+    for (int u = 0; u < TPS; ++u) {
+      const int j = first_block(i) + u;
+      ids[u] = (i < n_my && j < j1) ? __builtin_amdgcn_readfirstlane(trow[j]) : 0;
+    }
   };
 
-  // Issue the loads of this wave's i-th block into (kb, vb).  Past the wave's
-  // last block the resource is empty: the loads return zeros, touch nothing.
-  auto issue = [&](u32x4* kb, u32x4* vb, int i, int32_t bid) {
-    const bool live = i < n_my;
-    const int j = j0 + wave + kWaves * i;
-    const int ntok = min(L - j * BS, BS);
-    const bool id_ok = static_cast<uint64_t>(static_cast<int64_t>(bid)) < static_cast<uint64_t>(num_blocks);
-    bad = bad || (live && !id_ok);
-    const int nrec = (live && id_ok) ? ntok * G::kRowBytes : 0;
-    const int64_t tile = (int64_t(id_ok ? bid : 0) * H + h) * G::kTileBytes;
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(k_cache + tile), 0, nrec, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(v_cache + tile), 0, nrec, kBufferWord3);
+  // Issue the loads of stage i into (kb, vb).  A block past the stage's live
+  // range gets an empty resource: its loads return zeros and touch nothing.
+  auto issue = [&](u32x4* kb, u32x4* vb, int i, const int32_t* ids) {
 #pragma unroll
-    for (int t = 0; t < G::kLoads; ++t)
-      kb[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (t * 64 + lane) * 16, 0, kLoadPolicy));
+    for (int u = 0; u < TPS; ++u) {
+      const int j = first_block(i) + u;
+      const bool live = i < n_my && j < j1;
+      const int ntok = min(L - j * BS, BS);
+      const bool id_ok = static_cast<uint64_t>(static_cast<int64_t>(ids[u])) < static_cast<uint64_t>(num_blocks);
+      bad = bad || (live && !id_ok);
+      const int nrec = (live && id_ok) ? ntok * G::kRowBytes : 0;
+      const int64_t tile = (int64_t(id_ok ? ids[u] : 0) * H + h) * G::kTileBytes;
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(k_cache + tile), 0, nrec, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(v_cache + tile), 0, nrec, kBufferWord3);
 #pragma unroll
-    for (int t = 0; t < G::kLoads; ++t)
-      vb[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (t * 64 + lane) * 16, 0, kLoadPolicy));
+      for (int t = 0; t < G::kLoads; ++t)
+        kb[u * G::kLoads + t] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (t * 64 + lane) * 16, 0, kLoadPolicy));
+#pragma unroll
+      for (int t = 0; t < G::kLoads; ++t)
+        vb[u * G::kLoads + t] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (t * 64 + lane) * 16, 0, kLoadPolicy));
+    }
   };
 
-  // Fold this wave's i-th block into the row's running softmax state.
+  // Fold stage i into the row's running softmax state.
+  constexpr int kRows = TPS * G::kLoads;                  // token rows per lane per stage
   auto consume = [&](const u32x4* kb, const u32x4* vb, int i) {
-    const int j = j0 + wave + kWaves * i;
-    const int ntok = i < n_my ? L - j * BS : 0;           // rows at or past it are masked
-    float sc[G::kLoads];
+    float sc[kRows];
     float bm = kEmptyMax;
 #pragma unroll
-    for (int t = 0; t < G::kLoads; ++t) {
-      const float d = row_sum<G::kLpr>(dot16<DT>(qv, kb[t])) * scale_log2;
-      sc[t] = (t * G::kRpl + r < ntok) ? d : -__builtin_inff();
-      bm = fmaxf(bm, sc[t]);
+    for (int u = 0; u < TPS; ++u) {
+      const int j = first_block(i) + u;
+      const int ntok = (i < n_my && j < j1) ? L - j * BS : 0;   // rows at or past it are masked
+#pragma unroll
+      for (int t = 0; t < G::kLoads; ++t) {
+        const int x = u * G::kLoads + t;
+        const float d = row_sum<G::kLpr>(dot16<DT>(qv, kb[x])) * scale_log2;
+        sc[x] = (t * G::kRpl + r < ntok) ? d : -__builtin_inff();
+        bm = fmaxf(bm, sc[x]);
+      }
     }
     const float m_new = fmaxf(m, bm);
     const float alpha = exp2_fast(m - m_new);
@@ -273,35 +310,37 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
 #pragma unroll
     for (int e = 0; e < G::kEpl; ++e) acc[e] *= alpha;
 #pragma unroll
-    for (int t = 0; t < G::kLoads; ++t) {
-      const float pr = exp2_fast(sc[t] - m_new);
+    for (int x = 0; x < kRows; ++x) {
+      const float pr = exp2_fast(sc[x] - m_new);
       l += pr;
-      axpy16<DT>(pr, vb[t], acc);
+      axpy16<DT>(pr, vb[x], acc);
     }
     m = m_new;
   };
 
-  // Two-deep pipeline over buffers A and B: block i+1's loads are issued
-  // before block i is consumed.  The body has no branch between a buffer's
-  // loads and its consumer (a trailing odd step consumes an empty buffer,
-  // which leaves the state bit-for-bit unchanged), so the compiler cannot sink
-  // the loads below the consumer; the scheduling barriers keep the machine
-  // scheduler from doing the same inside the block.
+  // NST-deep pipeline over register buffers: stage i + NST - 1's loads are
+  // issued before stage i is consumed.  The body has no branch between a
+  // buffer's loads and its consumer (steps past the wave's last stage consume
+  // empty buffers, which leaves the state bit-for-bit unchanged), so the
+  // compiler cannot sink the loads below the consumer; the scheduling
+  // barriers keep the machine scheduler from doing the same inside a step.
   if (n_my > 0) {
-    u32x4 kA[G::kLoads], vA[G::kLoads], kB[G::kLoads], vB[G::kLoads];
-    int32_t t_next = table_at(1);
-    issue(kA, vA, 0, table_at(0));
-    for (int i = 0; i < n_my; i += 2) {
-      const int32_t t2 = table_at(i + 2);
-      issue(kB, vB, i + 1, t_next);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(kA, vA, i);
-      __builtin_amdgcn_sched_barrier(0);
-      t_next = table_at(i + 3);
-      issue(kA, vA, i + 2, t2);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(kB, vB, i + 1);
-      __builtin_amdgcn_sched_barrier(0);
+    u32x4 kb[NST][kRows], vb[NST][kRows];
+    int32_t ids[TPS];
+#pragma unroll
+    for (int b = 0; b < NST - 1; ++b) {
+      table_at(b, ids);
+      issue(kb[b], vb[b], b, ids);
+    }
+    for (int i = 0; i < n_my; i += NST) {
+#pragma unroll
+      for (int b = 0; b < NST; ++b) {
+        table_at(i + b + NST - 1, ids);
+        issue(kb[(b + NST - 1) % NST], vb[(b + NST - 1) % NST], i + b + NST - 1, ids);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(kb[b], vb[b], i + b);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
@@ -382,7 +421,8 @@ template <int DT, int D, int BS>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(unsigned(a.num_heads), unsigned(a.partitions), unsigned(a.num_seqs));
   constexpr int kWaves = waves_for<BS>();
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, kWaves>), grid, dim3(64 * kWaves), 0, stream, a.q,
+  constexpr int kTps = tiles_for<DT, D, BS>();
+  hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, kWaves, kTps, stages_for<DT, kTps>()>), grid, dim3(64 * kWaves), 0, stream, a.q,
                      static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
                      a.block_tables, a.context_lens, a.out, a.ws_m, a.ws_l, a.ws_acc, a.num_blocks,
                      a.max_blocks, a.part_blocks, a.partitions, a.scale_log2);

@@ -34,7 +34,7 @@ def declared_functions():
 def test_header_declares_the_two_calls():
     fns = declared_functions()
     assert {"paged_kv_write", "paged_attention_decode", "paged_attention_workspace_bytes",
-            "pkv_last_error"} <= set(fns)
+            "paged_attention_partition_size", "pkv_last_error"} <= set(fns)
 
 
 def test_library_exports_every_declared_function(libpath):
@@ -77,6 +77,7 @@ cases = [
   ("dec_neg_seqs", lambda: dec(B=-1), 1), ("dec_zero_seqs", lambda: dec(B=0, q=None), 0),
   ("dec_null_q", lambda: dec(q=None), 1), ("dec_null_tab", lambda: dec(tab=None), 1),
   ("dec_part", lambda: dec(part=100), 1), ("dec_part_neg", lambda: dec(part=-16), 1),
+  ("dec_part_auto_null_ws", lambda: dec(B=8, part=-1, ws=None), 3),
   ("dec_maxblocks", lambda: dec(mb=0), 1), ("dec_nblocks", lambda: dec(NB=0), 1),
   ("dec_scale", lambda: dec(scale=float("inf")), 1), ("dec_ws_null", lambda: dec(ws=None), 3),
   ("dec_ws_small", lambda: dec(wsb=ws - 1), 3), ("dec_grid", lambda: dec(B=70000), 2),
@@ -88,6 +89,11 @@ for name, call, want in cases:
     got = call()
     msg = lib.pkv_last_error().decode()
     print(f"{name} {got} {want} {msg!r}")
+lib.paged_attention_partition_size.argtypes = [i32] * 5
+lib.paged_attention_partition_size.restype = i32
+ps = lib.paged_attention_partition_size
+print("auto", ps(64, 40, 128, 16, -1), ps(8, 40, 2048, 16, -1), ps(4, 4, 7, 16, -1), ps(1, 1, 4096, 16, -1),
+      ps(8, 40, 2048, 16, 512), ps(8, 40, 2048, 16, 0), lib.paged_attention_workspace_bytes(8, 40, 128, 2048, 16, -1))
 print("ws", ws, lib.paged_attention_workspace_bytes(64, 40, 128, 128, 16, 0),
       lib.paged_attention_workspace_bytes(8, 40, 128, 2048, 16, 512))
 """
@@ -99,7 +105,13 @@ def test_validation_returns_status_before_any_launch(libpath):
                          timeout=120)
     assert res.returncode == 0, res.stderr
     lines = res.stdout.strip().splitlines()
-    for line in lines[:-1]:
+    auto = [int(x) for x in lines[-2].split()[1:]]
+    # >= 1024 rows: one pass; 320 rows of a 32768-token table: ceil(4096 / 320) = 13 partitions of
+    # ceil(32768 / 13) = 2521 -> 2560 tokens; a tiny table: no split; one row: 4096 / 4096 -> 512 tokens
+    assert auto[:6] == [0, 2560, 0, 512, 512, 0]
+    n_auto = 8 * 40 * 13
+    assert auto[6] == 2 * ((n_auto * 4 + 255) // 256 * 256) + n_auto * 128 * 4
+    for line in lines[:-2]:
         name, got, want, _ = line.split(" ", 3)
         assert got == want, line
     _, ws512, ws0, ws3 = lines[-1].split()
@@ -115,7 +127,7 @@ def test_error_messages_name_the_problem(libpath):
     env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1", CUDA_VISIBLE_DEVICES="-1")
     res = subprocess.run([sys.executable, "-c", CHILD, libpath], capture_output=True, text=True, env=env,
                          timeout=120)
-    msgs = {l.split(" ", 3)[0]: l.split(" ", 3)[3] for l in res.stdout.strip().splitlines()[:-1]}
+    msgs = {l.split(" ", 3)[0]: l.split(" ", 3)[3] for l in res.stdout.strip().splitlines()[:-2]}
     assert "head_dim 96" in msgs["dec_head_dim"]
     assert "workspace" in msgs["dec_ws_small"]
     assert "partition_size 100" in msgs["dec_part"]

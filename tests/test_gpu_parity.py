@@ -143,7 +143,7 @@ def test_edge_lengths_every_shape(pkv, dt, D, bs):
     c = P.Case(rng, lens, H=3, D=D, bs=bs, dtype="bf16" if dt == "bf16" else dt)
     ref = oracle.decode(c.q, c.k_pool, c.v_pool, c.tables, c.context_lens, c.scale, bs, c.dtype)
     q, kc, vc, tab, lens_t = case_on_gpu(c)
-    for part in (0, bs, 4 * bs, 512):
+    for part in (0, bs, 4 * bs, 512, pkv.PARTITION_AUTO):
         say(f"[edge] {dt} D={D} bs={bs} partition={part} lens={lens}")
         out = pkv.paged_attention_decode(q, kc, vc, tab, lens_t, c.scale, partition_size=part)
         torch.cuda.synchronize()
@@ -157,7 +157,7 @@ def test_split_and_single_pass_agree_long_context(pkv):
     w = W.make_workload(meta, "cuda")
     pkv.paged_kv_write(w.k_new, w.v_new, w.slot_mapping, w.k_cache, w.v_cache)
     outs = {}
-    for part in (512, 0, 16, 4096):
+    for part in (512, 0, 16, 4096, pkv.PARTITION_AUTO):
         say(f"[split] B=3 L=(32768, 20000, 777) H=40 D=128 bf16 partition={part}")
         outs[part] = out_host(pkv.paged_attention_decode(w.q, w.k_cache, w.v_cache, w.block_tables,
                                                          w.context_lens, meta.cfg.scale, partition_size=part))
