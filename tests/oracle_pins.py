@@ -395,3 +395,200 @@ PINS = [pin_block_counts, pin_storage_upcast, pin_round_to_storage, pin_slot_exa
         pin_write_then_read, pin_write_bitwise, pin_brute_force, pin_pages_tables,
         pin_permutation_invariance, pin_poison_invariance, pin_closed_forms,
         pin_split_equals_single, pin_prefix_sharing]
+
+
+# ---------------------------------------------------------------- block pool pins
+# Each takes the block-pool module (oracle.block_manager) and the oracle module.
+
+def _front(first, num_blocks, rest_seed=0):
+    """A free order that starts with ``first`` (a list) and continues with the other ids shuffled."""
+    rest = [b for b in np.random.default_rng(rest_seed).permutation(num_blocks).tolist() if b not in first]
+    return list(first) + rest
+
+
+def pin_pool_block42_flow(bm, o):
+    g = golden("block_pool.json")["block42"]
+    bs = g["block_size"]
+    pool = bm.BlockPool(64, bs, _front([g["first_free"], 7], 64))
+    assert pool.allocate("req", g["prompt_tokens"]) == g["table_after_prefill"]
+    slots, copies = pool.append_slots("req", 1)
+    assert slots == [g["first_decode_slot"]] and copies == []
+    slots, _ = pool.append_slots("req", g["block_full_after_tokens"] - g["prompt_tokens"] - 1)
+    assert slots == list(range(42 * bs + 7, 42 * bs + bs)) and pool.table("req") == [42]
+    slots, copies = pool.append_slots("req", 1)                  # token 16: a new block
+    assert pool.table("req") == [42, 7] and slots == [7 * bs] and copies == []
+    free_before = pool.num_free()
+    assert pool.free_sequence("req") == [42, 7] and pool.num_free() == free_before + 2
+    assert pool.allocate("next", 20) == [42, 7]                   # immediately reused
+
+
+def pin_pool_prefix_full_block(bm, o):
+    g = golden("block_pool.json")["prefix_sharing"]
+    bs, shared = g["block_size"], g["shared_block"]
+    own = g["own_blocks"]
+    pool = bm.BlockPool(100, bs, _front([shared, own["A"], own["B"], own["C"]], 100))
+    pool.allocate("prompt", bs)                                   # a prefix that fills block 5
+    for r in ("A", "B", "C"):
+        pool.fork("prompt", r)
+    pool.free_sequence("prompt")
+    assert pool.refcount[shared] == g["refcount"]
+    for r in ("A", "B", "C"):
+        slots, copies = pool.append_slots(r, 1)
+        assert copies == [] and slots == [own[r] * bs]
+        assert pool.table(r) == [shared, own[r]]
+    assert pool.refcount[shared] == 3
+
+
+def pin_pool_copy_on_write(bm, o):
+    g = golden("block_pool.json")["prefix_sharing"]
+    bs, shared, n = g["block_size"], g["shared_block"], g["short_prompt_tokens"]
+    pool = bm.BlockPool(100, bs, _front([shared, 40, 41, 42], 100))
+    pool.allocate("prompt", n)
+    for r in ("A", "B", "C"):
+        pool.fork("prompt", r)
+    assert pool.refcount[shared] == 4
+    slots, copies = pool.append_slots("A", 1)                    # write into the shared block: copy
+    assert copies == [(shared, 40)] and slots == [40 * bs + n]
+    assert pool.table("A") == [40] and pool.table("B") == [shared] and pool.refcount[shared] == 3
+    slots, copies = pool.append_slots("A", 2)                    # A's block is private now
+    assert copies == [] and slots == [40 * bs + n + 1, 40 * bs + n + 2]
+    assert pool.append_slots("B", 1)[1] == [(shared, 41)]
+    assert pool.append_slots("C", 1)[1] == [(shared, 42)]
+    assert pool.refcount[shared] == 1 and pool.table("prompt") == [shared]
+    # once only one table holds it, its owner writes in place
+    assert pool.append_slots("prompt", 1) == ([shared * bs + n], [])
+
+
+def pin_pool_parallel_sampling(bm, o):
+    g = golden("block_pool.json")["parallel_sampling"]
+    bs, L, n = g["block_size"], g["prompt_tokens"], g["samples"]
+    pool = bm.BlockPool(64, bs)
+    pool.allocate(0, L)
+    for s in range(1, n):
+        pool.fork(0, s)
+    copies = []
+    for s in range(n):
+        copies += pool.append_slots(s, 1)[1]
+    in_use = 64 - pool.num_free()
+    assert in_use == g["blocks_shared_after_one_token"] and len(copies) == n - 1
+    assert n * -(-(L + 1) // bs) == g["blocks_unshared"]
+    full = pool.table(0)[:L // bs]
+    assert all(pool.table(s)[:L // bs] == full for s in range(n))          # full prompt blocks stay shared
+    assert len({pool.table(s)[-1] for s in range(n)}) == n                  # each sample owns its last block
+
+
+def _check_pool_invariants(pool):
+    count = [0] * pool.num_blocks
+    for seq, t in pool.tables.items():
+        assert len(t) == -(-pool.tokens[seq] // pool.block_size), seq
+        for b in t:
+            count[b] += 1
+    assert count == pool.refcount
+    free = set(pool.free)
+    assert len(free) == len(pool.free)
+    assert all((count[b] == 0) == (b in free) for b in range(pool.num_blocks))
+
+
+def _random_ops(bm, rng, pool, steps, on=None):
+    """Random allocate / fork / append / free on ``pool``; ``on`` maps event names to callbacks."""
+    on = on or {}
+    live, next_id = [], 0
+
+    def event(name, *args):
+        if name in on:
+            on[name](*args)
+
+    for _ in range(steps):
+        r = rng.random()
+        try:
+            if r < 0.25 or not live:
+                pool.allocate(next_id, int(rng.integers(1, 60)))
+                event("allocate", next_id)
+                live.append(next_id)
+                next_id += 1
+            elif r < 0.4:
+                parent = live[int(rng.integers(len(live)))]
+                pool.fork(parent, next_id)
+                event("fork", parent, next_id)
+                live.append(next_id)
+                next_id += 1
+            elif r < 0.85:
+                s = live[int(rng.integers(len(live)))]
+                slots, copies = pool.append_slots(s, int(rng.integers(1, 20)))
+                event("append", s, slots, copies)
+            else:
+                s = live.pop(int(rng.integers(len(live))))
+                pool.free_sequence(s)
+                event("free", s)
+        except bm.OutOfBlocks:
+            if live:
+                s = live.pop(0)
+                pool.free_sequence(s)
+                event("free", s)
+        _check_pool_invariants(pool)
+        yield live
+
+
+def pin_pool_invariants(bm, o):
+    rng = np.random.default_rng(21)
+    pool = bm.BlockPool(48, 16, rng.permutation(48))
+    for live in _random_ops(bm, rng, pool, 400):
+        for s in live:                          # every token's slot index falls inside the table
+            assert pool.tokens[s] <= len(pool.table(s)) * pool.block_size
+
+
+def pin_pool_contents(bm, o):
+    """Data-level check: sequences keep exactly their own tokens through shared prefixes,
+    copy-on-write, appends and frees (copies via copy_blocks, writes via the oracle's kv_write)."""
+    rng = np.random.default_rng(22)
+    NB, H, bs, D = 40, 2, 8, 4
+    pool = bm.BlockPool(NB, bs, rng.permutation(NB))
+    st = {"k": np.full((NB, H, bs, D), np.nan, dtype=np.float32),
+          "v": np.full((NB, H, bs, D), np.nan, dtype=np.float32)}
+    expect = {}
+
+    def write(seq, slots):
+        kn = rng.standard_normal((len(slots), H, D)).astype(np.float32)
+        vn = rng.standard_normal((len(slots), H, D)).astype(np.float32)
+        st["k"], st["v"] = o.kv_write(kn, vn, np.array(slots), st["k"], st["v"], bs)
+        old_k, old_v = expect.get(seq, (np.zeros((0, H, D), np.float32), np.zeros((0, H, D), np.float32)))
+        expect[seq] = (np.concatenate([old_k, kn]), np.concatenate([old_v, vn]))
+
+    def on_allocate(seq):
+        t = pool.table(seq)
+        write(seq, [t[i // bs] * bs + i % bs for i in range(pool.tokens[seq])])
+
+    def on_append(seq, slots, copies):
+        st["k"], st["v"] = bm.copy_blocks(st["k"], st["v"], copies)
+        write(seq, slots)
+
+    on = {"allocate": on_allocate, "append": on_append,
+          "fork": lambda p, c: expect.__setitem__(c, expect[p]), "free": lambda s: expect.pop(s)}
+    for live in _random_ops(bm, rng, pool, 300, on):
+        for s in live:
+            t, L = pool.table(s), pool.tokens[s]
+            K = o.gather_sequence(st["k"], t, L, bs, "f32")
+            V = o.gather_sequence(st["v"], t, L, bs, "f32")
+            assert np.array_equal(K, expect[s][0].transpose(1, 0, 2)), s
+            assert np.array_equal(V, expect[s][1].transpose(1, 0, 2)), s
+
+
+def pin_copy_blocks(bm, o):
+    rng = np.random.default_rng(23)
+    NB, H, bs, D = 12, 3, 16, 8
+    k = rng.standard_normal((NB, H, bs, D)).astype(np.float32)
+    v = rng.standard_normal((NB, H, bs, D)).astype(np.float32)
+    k[2, 1, 5, 3] = np.float32(np.nan)
+    k[2, 0, 0, 0] = np.float32(-0.0)
+    pairs = [(2, 9), (4, 0), (2, 11)]
+    k2, v2 = bm.copy_blocks(k, v, pairs)
+    for s, d in pairs:
+        assert np.array_equal(k2[d].view(np.uint32), k[s].view(np.uint32))
+        assert np.array_equal(v2[d].view(np.uint32), v[s].view(np.uint32))
+    untouched = [b for b in range(NB) if b not in (9, 0, 11)]
+    assert np.array_equal(k2[untouched].view(np.uint32), k[untouched].view(np.uint32))
+    assert np.array_equal(v2[untouched].view(np.uint32), v[untouched].view(np.uint32))
+
+
+POOL_PINS = [pin_pool_block42_flow, pin_pool_prefix_full_block, pin_pool_copy_on_write,
+             pin_pool_parallel_sampling, pin_pool_invariants, pin_pool_contents, pin_copy_blocks]

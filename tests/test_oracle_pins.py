@@ -161,3 +161,147 @@ def test_planted_mistake_is_caught(name, monkeypatch):
         except Exception:          # an assertion, or the mistake breaking the computation outright
             failed.append(pin.__name__)
     assert failed, f"no pin catches: {name}"
+
+
+# ------------------------------------------------------------- block pool: pins and planted mistakes
+
+import oracle.block_manager as BM
+
+
+@pytest.mark.parametrize("pin", P.POOL_PINS, ids=lambda f: f.__name__)
+def test_pool_pin(pin):
+    pin(BM, O)
+
+
+def _orig(name):
+    return BM.__dict__["_orig_" + name]
+
+
+def _append_no_cow(self, seq, n):
+    bs, table = self.block_size, self.tables[seq]
+    slots = []
+    for t in range(self.tokens[seq], self.tokens[seq] + int(n)):
+        j, off = divmod(t, bs)
+        if j == len(table):
+            table.append(self._take())
+        slots.append(table[j] * bs + off)
+    self.tokens[seq] += int(n)
+    return slots, []
+
+
+def _append_cow_keeps_count(self, seq, n):
+    rc = self.refcount
+    before = list(rc)
+    slots, copies = _orig("append_slots")(self, seq, n)
+    for s, _ in copies:
+        rc[s] = before[s]                 # forgets that the writer no longer references the source
+    return slots, copies
+
+
+def _append_reversed_copies(self, seq, n):
+    slots, copies = _orig("append_slots")(self, seq, n)
+    return slots, [(d, s) for s, d in copies]
+
+
+def _append_late_block(self, seq, n):
+    bs, table = self.block_size, self.tables[seq]
+    slots, copies = [], []
+    for t in range(self.tokens[seq], self.tokens[seq] + int(n)):
+        j, off = divmod(t, bs)
+        if j == len(table) and off > 0:   # waits one token too long before adding a block
+            table.append(self._take())
+        jj = min(j, len(table) - 1)
+        slots.append(table[jj] * bs + off)
+    self.tokens[seq] += int(n)
+    return slots, copies
+
+
+def _append_offset_off_by_one(self, seq, n):
+    slots, copies = _orig("append_slots")(self, seq, n)
+    return [s + 1 for s in slots], copies
+
+
+def _free_keeps_blocks(self, seq):
+    for b in self.tables.pop(seq):
+        self.refcount[b] -= 1
+    del self.tokens[seq]
+    return []
+
+
+def _free_to_back(self, seq):
+    released = []
+    for b in self.tables.pop(seq):
+        self.refcount[b] -= 1
+        if self.refcount[b] == 0:
+            released.append(b)
+    del self.tokens[seq]
+    self.free.extend(released)
+    return released
+
+
+def _free_ignores_sharing(self, seq):
+    released = list(self.tables.pop(seq))
+    for b in released:
+        self.refcount[b] = 0
+    del self.tokens[seq]
+    self.free[:0] = released
+    return released
+
+
+def _fork_no_refcount(self, parent, child):
+    self.tables[child] = list(self.tables[parent])
+    self.tokens[child] = self.tokens[parent]
+
+
+def _allocate_floor(self, seq, num_tokens):
+    need = max(1, int(num_tokens) // self.block_size)
+    if need > len(self.free):
+        raise BM.OutOfBlocks("")
+    self.tables[seq] = [self._take() for _ in range(need)]
+    self.tokens[seq] = int(num_tokens)
+    return list(self.tables[seq])
+
+
+def _copy_k_only(k_cache, v_cache, copies):
+    k2, _ = _orig("copy_blocks")(k_cache, v_cache, copies)
+    return k2, np.array(v_cache, copy=True)
+
+
+def _copy_backwards(k_cache, v_cache, copies):
+    return _orig("copy_blocks")(k_cache, v_cache, [(d, s) for s, d in copies]) if copies else \
+        (np.array(k_cache, copy=True), np.array(v_cache, copy=True))
+
+
+POOL_MUTANTS = {
+    "append never copies a shared block": ("BlockPool.append_slots", _append_no_cow),
+    "copy-on-write keeps the source's count": ("BlockPool.append_slots", _append_cow_keeps_count),
+    "copy pairs reversed": ("BlockPool.append_slots", _append_reversed_copies),
+    "new block one token late": ("BlockPool.append_slots", _append_late_block),
+    "slot offset off by one": ("BlockPool.append_slots", _append_offset_off_by_one),
+    "free never returns blocks": ("BlockPool.free_sequence", _free_keeps_blocks),
+    "free returns blocks to the back": ("BlockPool.free_sequence", _free_to_back),
+    "free ignores other holders": ("BlockPool.free_sequence", _free_ignores_sharing),
+    "fork does not count references": ("BlockPool.fork", _fork_no_refcount),
+    "allocate floors the block count": ("BlockPool.allocate", _allocate_floor),
+    "copy_blocks copies K only": ("copy_blocks", _copy_k_only),
+    "copy_blocks copies backwards": ("copy_blocks", _copy_backwards),
+}
+
+
+@pytest.mark.parametrize("name", sorted(POOL_MUTANTS))
+def test_pool_planted_mistake_is_caught(name, monkeypatch):
+    where, bad = POOL_MUTANTS[name]
+    if where.startswith("BlockPool."):
+        attr = where.split(".")[1]
+        monkeypatch.setitem(BM.__dict__, "_orig_" + attr, getattr(BM.BlockPool, attr))
+        monkeypatch.setattr(BM.BlockPool, attr, bad)
+    else:
+        monkeypatch.setitem(BM.__dict__, "_orig_" + where, getattr(BM, where))
+        monkeypatch.setattr(BM, where, bad)
+    failed = []
+    for pin in P.POOL_PINS:
+        try:
+            pin(BM, O)
+        except Exception:
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches: {name}"
