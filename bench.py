@@ -148,12 +148,146 @@ def copy_calibration(mib):
                       "launches": 5}), flush=True)
 
 
+def parallel_sampling(args):
+    """Decode step of parallel sampling over shared prompts: the block pool reserves each sample's new
+    slot (copying the shared, partly filled last block of a prompt for all but its last writer), then
+    copy_blocks + paged_kv_write + paged_attention_decode run on the GPU."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_383_amd as pkv
+    import workloads as W
+    cfg = W.SamplingConfig()
+    dev = torch.device("cuda:0")
+    es = elem_bytes(cfg.dtype)
+    H, D, bs = cfg.num_heads, cfg.head_dim, cfg.block_size
+    block_bytes = H * bs * D * es
+    dt = W.torch_dtype(cfg.dtype)
+    sets = []
+    for r in range(2):                                   # two independent pools, > 256 MB each
+        lens, nb, order = W.sampling_prompts(cfg, cfg.seed + r)
+        pool = pkv.BlockPool(nb, bs, order)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(cfg.seed + r)
+        kc = torch.empty((nb, H, bs, D), dtype=dt, device=dev)
+        vc = torch.empty_like(kc)
+        W._randn_into(kc, gen, 1.0, 1024)
+        W._randn_into(vc, gen, 1.0, 1024)
+        seqs, slots, copies = [], [], []
+        for p, L in enumerate(lens.tolist()):
+            pool.allocate(p * cfg.samples, L)            # prompt K/V: the random pool contents
+            for s in range(1, cfg.samples):
+                pool.fork(p * cfg.samples, p * cfg.samples + s)
+            for s in range(cfg.samples):
+                sl, cp = pool.append_slots(p * cfg.samples + s, 1)
+                seqs.append(p * cfg.samples + s)
+                slots += sl.tolist()
+                copies += cp.tolist()
+        width = (cfg.max_len + 1 + bs - 1) // bs
+        tables, ctx = pool.build_tables(seqs, width)
+        B = len(seqs)
+        q = torch.randn((B, H, D), generator=gen, device=dev).to(dt)
+        kn = torch.randn((B, H, D), generator=gen, device=dev).to(dt)
+        vn = torch.randn((B, H, D), generator=gen, device=dev).to(dt)
+        sets.append(dict(kc=kc, vc=vc, q=q, kn=kn, vn=vn, out=torch.empty_like(q),
+                         slots=torch.tensor(slots, dtype=torch.int64, device=dev),
+                         copies=torch.tensor(copies, dtype=torch.int64, device=dev).reshape(-1, 2),
+                         tables=torch.from_numpy(tables).to(dev), lens=torch.from_numpy(ctx).to(dev),
+                         ctx=ctx, pool=pool))
+    ws = torch.zeros(1, dtype=torch.uint8, device=dev)
+    B = len(sets[0]["ctx"])
+    n_copy = sets[0]["copies"].shape[0]
+    ctx = sets[0]["ctx"].astype(np.int64)
+    decode_b = int(ctx.sum()) * H * D * 2 * es + B * H * D * 2 * es + 4 * int(((ctx + bs - 1) // bs).sum()) + 4 * B
+    write_b = 2 * B * H * D * es * 2 + 8 * B
+    copy_b = n_copy * 2 * 2 * block_bytes + 16 * n_copy
+    tab0 = sets[0]["tables"].cpu().numpy()
+    unique_b = int(np.unique(tab0[tab0 >= 0]).size) * 2 * block_bytes      # each shared block once
+    log(f"{cfg.name}: {cfg.prompts} prompts x {cfg.samples} samples, {n_copy} block copies per step, "
+        f"sum(L) = {int(ctx.sum())}")
+
+    def copy(i):
+        st = sets[i % 2]
+        pkv.paged_kv_copy_blocks(st["kc"], st["vc"], st["copies"])
+
+    def write(i):
+        st = sets[i % 2]
+        pkv.paged_kv_write(st["kn"], st["vn"], st["slots"], st["kc"], st["vc"])
+
+    def decode(i):
+        st = sets[i % 2]
+        pkv.paged_attention_decode(st["q"], st["kc"], st["vc"], st["tables"], st["lens"], cfg.scale,
+                                   out=st["out"], workspace=ws)
+
+    for i in range(args.warmup):
+        copy(i)
+        write(i)
+        decode(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        copy(i)
+        write(i)
+        decode(i)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+
+    def timed(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(n):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    decode_us, copy_us = timed(decode, args.steps), timed(copy, args.steps)
+    # the copy kernel at scale: every block of the first 1.3 GB of the pool copied to the rest
+    big = sets[0]
+    nb = big["kc"].shape[0]
+    n_big = min(nb // 2, 4096)
+    pairs = torch.stack([torch.arange(n_big), torch.arange(n_big) + nb - n_big], 1).to(dev)
+    big_us = timed(lambda i: pkv.paged_kv_copy_blocks(big["kc"], big["vc"], pairs), 10)
+    big_b = n_big * 2 * 2 * block_bytes + 16 * n_big
+    achieved = decode_b / (decode_us * 1e-6) / 1e9
+    step_b = decode_b + write_b + copy_b
+    log(f"step {step_s * 1e6:.1f} us; decode {decode_us:.1f} us = {achieved:.0f} GB/s; copies {copy_us:.1f} us; "
+        f"copy kernel at scale {n_big} pairs {big_us:.1f} us = {big_b / big_us / 1e3:.0f} GB/s")
+    rec = {
+        "metric": METRIC, "value": round(step_b / step_s / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "num_seqs": B, "prompts": cfg.prompts, "samples": cfg.samples,
+                   "num_heads": H, "head_dim": D, "block_size": bs, "sum_context_tokens": int(ctx.sum()),
+                   "block_copies_per_step": n_copy,
+                   "step": "paged_kv_copy_blocks + paged_kv_write + paged_attention_decode",
+                   "step_algorithmic_bytes": step_b},
+        "tokens_heads_per_s": round(int(ctx.sum()) * H / step_s, 1),
+        "kernels_us": {"paged_kv_copy_blocks": round(copy_us, 2), "paged_attention_decode": round(decode_us, 2)},
+        "copy_kernel_at_scale": {"pairs": n_big, "bytes": big_b, "us": round(big_us, 2),
+                                 "GB_per_s": round(big_b / big_us / 1e3, 1),
+                                 "frac": round(big_b / big_us / 1e3 / PEAK_HBM_GBS, 4)},
+        "roofline": {"kernel": "paged_attention_decode (decode_partition_kernel)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": decode_b, "mean_launch_us": round(decode_us, 2),
+                     "note": "algorithmic bytes count every sample's read of a shared prompt block; the blocks "
+                             "themselves hold unique_kv_bytes, so caches may serve repeat reads"},
+        "unique_kv_bytes": unique_b,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--workload", choices=["decode", "parallel_sampling"], default="decode",
+                    help="decode: one decode step of --config; parallel_sampling: a decode step over "
+                         "prompts shared by parallel samples (copy-on-write copies + write + decode)")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="split-context partition in tokens (0 = one pass); default: the library's choice")
     ap.add_argument("--rotate", type=int, default=None, help="independent input copies cycled over")
@@ -178,6 +312,9 @@ def main():
     if not os.path.exists(b.LIB_PATH):
         b.build()
     pkv.lib()
+    if args.workload == "parallel_sampling":
+        parallel_sampling(args)
+        return
 
     dev = torch.device("cuda:0")
     meta = W.make_metadata(args.config)

@@ -71,7 +71,8 @@ typedef enum {
   PKV_EINVAL = 1,        /* bad argument: null pointer, negative or inconsistent size      */
   PKV_EUNSUPPORTED = 2,  /* valid but not built: dtype, head_dim, block_size, grid too big */
   PKV_EWORKSPACE = 3,    /* workspace missing or smaller than paged_attention_workspace_bytes */
-  PKV_EHIP = 4           /* the HIP runtime refused a launch or a copy                      */
+  PKV_EHIP = 4,          /* the HIP runtime refused a launch or a copy                      */
+  PKV_ENOSPACE = 5       /* block pool: too few free blocks (nothing was changed)          */
 } pkv_status;
 
 /*
@@ -155,8 +156,92 @@ int paged_attention_decode(const void* q, const void* k_cache, const void* v_cac
                            int32_t dtype, void* out, void* workspace, size_t workspace_bytes,
                            int32_t partition_size, void* stream);
 
+/*
+ * paged_kv_copy_blocks -- copy whole physical blocks, K and V: for every pair
+ * i, block block_mapping[2i+1] of each pool receives the contents of block
+ * block_mapping[2i].  This is the copy in copy-on-write ([explain] Step 9: a
+ * request about to write into a block it shares first gets a private copy, and
+ * its table is pointed at the copy); pkv_pool_append_slots reports the pairs.
+ * A block is every head and slot: num_heads * block_size * head_dim elements,
+ * one contiguous run per pool.  The copy moves stored bits and is exact.
+ *
+ *   k_cache,
+ *   v_cache        [num_blocks, num_heads, block_size, head_dim], dtype
+ *   block_mapping  [num_pairs, 2] int64 (source, destination), read
+ * Destinations must be distinct and none may also be a source (the copies run
+ * concurrently); PKV_DEBUG=1 checks this and the id range on the host.  A pair
+ * with an id outside [0, num_blocks) is skipped by the kernel.  Returns PKV_OK,
+ * or an error status with nothing launched.  num_pairs == 0 is a no-op.
+ */
+int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int64_t num_pairs,
+                         int64_t num_blocks, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                         int32_t dtype, void* stream);
+
 /* Text of the calling thread's last non-OK status (empty string if none). */
 const char* pkv_last_error(void);
+
+/*
+ * ---- Block pool: host-side bookkeeping of physical blocks ----
+ *
+ * The scheduler's side of paged KV memory ([card] "OS paging과 같은 발상",
+ * "vLLM에서의 위치"; [explain] Steps 5-9).  A pool hands out block ids for
+ * sequences named by caller-chosen int64 ids, keeps a block table and a token
+ * count per sequence, and a reference count per block (the number of tables
+ * holding it).  It touches no GPU memory: its outputs (tables, context lengths,
+ * slot ids, copy pairs) are host arrays for the caller to upload and pass to
+ * paged_kv_copy_blocks, paged_kv_write and paged_attention_decode.
+ *
+ * Policy.  Token t of a sequence lives in logical block t / block_size.
+ * Allocation takes blocks from the front of an ordered free list; blocks whose
+ * count drops to zero return to the front in table order, so the next request
+ * receives the space just released ([explain] Steps 7-8).  A block is copied
+ * before a write only while another table still holds it; the last holder
+ * writes in place.  Every call is all-or-nothing: PKV_ENOSPACE and PKV_EINVAL
+ * leave the pool unchanged.  A pool is not thread-safe; calls on one pool must
+ * not overlap.  All pointers here are HOST pointers.
+ */
+typedef struct pkv_block_pool pkv_block_pool;
+
+/* A pool of num_blocks blocks of block_size tokens; free_order (may be NULL =
+ * 0, 1, 2, ...) lists every block id once, front first.  NULL on bad input. */
+pkv_block_pool* pkv_pool_create(int64_t num_blocks, int32_t block_size, const int32_t* free_order);
+void pkv_pool_destroy(pkv_block_pool* pool);
+
+/* New sequence `seq` holding num_tokens tokens in ceil(num_tokens / block_size)
+ * fresh blocks ([explain] Step 6: blocks are allocated at the start of prefill). */
+int pkv_pool_allocate(pkv_block_pool* pool, int64_t seq, int64_t num_tokens);
+
+/* New sequence `child` sharing all of `parent`'s blocks (each gains a
+ * reference): a shared prompt prefix or parallel samples ([explain] Step 9). */
+int pkv_pool_fork(pkv_block_pool* pool, int64_t parent, int64_t child);
+
+/* Reserve slots for n new tokens of `seq`.  slots_out[n] receives each token's
+ * flat slot (block * block_size + offset) for paged_kv_write.  A new block is
+ * appended at each block boundary ([explain] Step 6).  If the partly filled
+ * last block is shared, it is replaced by a fresh block and the pair (old, new)
+ * goes to copies_out (int64 [max_copies, 2]); *num_copies receives the count
+ * (0 or 1).  The copies must run (paged_kv_copy_blocks) before the write. */
+int pkv_pool_append_slots(pkv_block_pool* pool, int64_t seq, int64_t n, int64_t* slots_out,
+                          int64_t* copies_out, int64_t max_copies, int64_t* num_copies);
+
+/* Drop `seq`; blocks no other table holds return to the free list ([explain]
+ * Step 7: released blocks are immediately reusable). */
+int pkv_pool_free(pkv_block_pool* pool, int64_t seq);
+
+/* Padded int32 block tables [n, width] (unused entries -1) and int32 context
+ * lengths [n] of the listed sequences, ready for paged_attention_decode. */
+int pkv_pool_build_tables(const pkv_block_pool* pool, const int64_t* seqs, int32_t n, int32_t width,
+                          int32_t* tables_out, int32_t* lens_out);
+
+/* Queries: free block count; a block's reference count (-1 for a bad id);
+ * a sequence's token count (-1 if unknown); a sequence's table (writes up to
+ * cap ids, returns its length, -1 if unknown); the free list front first
+ * (writes up to cap ids, returns its length). */
+int64_t pkv_pool_num_free(const pkv_block_pool* pool);
+int32_t pkv_pool_refcount(const pkv_block_pool* pool, int64_t block);
+int64_t pkv_pool_num_tokens(const pkv_block_pool* pool, int64_t seq);
+int64_t pkv_pool_table(const pkv_block_pool* pool, int64_t seq, int32_t* out, int64_t cap);
+int64_t pkv_pool_free_list(const pkv_block_pool* pool, int32_t* out, int64_t cap);
 
 #ifdef __cplusplus
 }

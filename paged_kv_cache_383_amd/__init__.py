@@ -13,6 +13,9 @@ If the library is not built, every call raises.
                                     max_blocks_per_seq, block_size, partition_size)
     paged_attention_partition_size(num_seqs, num_heads, max_blocks_per_seq, block_size,
                                    partition_size)
+    paged_kv_copy_blocks(k_cache, v_cache, block_mapping)
+    BlockPool(num_blocks, block_size, free_order=None): allocate, fork, append_slots,
+        free_sequence, build_tables, table, num_tokens, num_free, refcount, free_list
 
 partition_size: tokens per split-context partition, 0 for one pass per
 sequence, or PARTITION_AUTO (the default) to let the library choose.
@@ -23,8 +26,9 @@ import ctypes
 import os
 
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
-PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = 0, 1, 2, 3, 4
-STATUS_NAMES = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP"}
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP, PKV_ENOSPACE = 0, 1, 2, 3, 4, 5
+STATUS_NAMES = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP",
+                5: "PKV_ENOSPACE"}
 PARTITION_AUTO = -1            # let the library choose the split-context partition
 DEFAULT_PARTITION = PARTITION_AUTO
 
@@ -36,6 +40,10 @@ class PagedKVError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
         self.status = status
+
+
+class OutOfBlocks(PagedKVError):
+    """The block pool has too few free blocks (PKV_ENOSPACE); the pool is unchanged."""
 
 
 def lib() -> ctypes.CDLL:
@@ -56,6 +64,21 @@ def lib() -> ctypes.CDLL:
         L.paged_attention_decode.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i64,
                                              ctypes.c_float, i32, vp, vp, sz, i32, vp]
         L.paged_attention_decode.restype = ctypes.c_int
+        L.paged_kv_copy_blocks.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, vp]
+        L.paged_kv_copy_blocks.restype = ctypes.c_int
+        pool_fns = {
+            "pkv_pool_create": ([i64, i32, vp], vp), "pkv_pool_destroy": ([vp], None),
+            "pkv_pool_allocate": ([vp, i64, i64], ctypes.c_int), "pkv_pool_fork": ([vp, i64, i64], ctypes.c_int),
+            "pkv_pool_append_slots": ([vp, i64, i64, vp, vp, i64, vp], ctypes.c_int),
+            "pkv_pool_free": ([vp, i64], ctypes.c_int),
+            "pkv_pool_build_tables": ([vp, vp, i32, i32, vp, vp], ctypes.c_int),
+            "pkv_pool_num_free": ([vp], i64), "pkv_pool_refcount": ([vp, i64], i32),
+            "pkv_pool_num_tokens": ([vp, i64], i64), "pkv_pool_table": ([vp, i64, vp, i64], i64),
+            "pkv_pool_free_list": ([vp, vp, i64], i64),
+        }
+        for name, (args, res) in pool_fns.items():
+            getattr(L, name).argtypes = args
+            getattr(L, name).restype = res
         L.pkv_last_error.argtypes = []
         L.pkv_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -67,6 +90,8 @@ def last_error() -> str:
 
 
 def _check(status: int):
+    if status == PKV_ENOSPACE:
+        raise OutOfBlocks(status, last_error())
     if status != PKV_OK:
         raise PagedKVError(status, last_error())
 
@@ -160,3 +185,100 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
                                             workspace.data_ptr(), ws_bytes, partition_size,
                                             _stream(q.device)))
     return out
+
+
+def paged_kv_copy_blocks(k_cache, v_cache, block_mapping):
+    """Block block_mapping[i, 1] of both pools receives block block_mapping[i, 0] (int64 [N, 2])."""
+    import torch
+    _device_tensor("k_cache", k_cache, None, 4)
+    _device_tensor("v_cache", v_cache, k_cache.dtype, 4)
+    _device_tensor("block_mapping", block_mapping, torch.int64, 2)
+    if v_cache.shape != k_cache.shape or block_mapping.shape[1] != 2:
+        raise ValueError("caches must match and block_mapping must be [N, 2]")
+    NB, H, bs, D = k_cache.shape
+    with torch.cuda.device(k_cache.device):
+        _check(lib().paged_kv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), block_mapping.data_ptr(),
+                                          block_mapping.shape[0], NB, H, D, bs, _dtype_code(k_cache),
+                                          _stream(k_cache.device)))
+
+
+class BlockPool:
+    """Host-side block pool of the C library (pkv_pool_*): allocation, forks, slot reservation with
+    copy-on-write, freeing.  Sequence ids are Python ints.  Outputs are host NumPy arrays."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        import numpy as np
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        order = None
+        if free_order is not None:
+            order = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+            if order.shape != (self.num_blocks,):
+                raise ValueError("free_order must list num_blocks ids")
+        ptr = lib().pkv_pool_create(self.num_blocks, self.block_size,
+                                    None if order is None else order.ctypes.data)
+        if not ptr:
+            raise PagedKVError(PKV_EINVAL, last_error())
+        self._h = ctypes.c_void_p(ptr)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.pkv_pool_destroy(h)
+            self._h = None
+
+    def allocate(self, seq: int, num_tokens: int):
+        _check(lib().pkv_pool_allocate(self._h, int(seq), int(num_tokens)))
+        return self.table(seq)
+
+    def fork(self, parent: int, child: int):
+        _check(lib().pkv_pool_fork(self._h, int(parent), int(child)))
+
+    def append_slots(self, seq: int, n: int):
+        """(slots int64 [n], copies int64 [k, 2]) for n new tokens of ``seq``."""
+        import numpy as np
+        slots = np.empty(max(int(n), 1), dtype=np.int64)
+        copies = np.empty((1, 2), dtype=np.int64)
+        k = ctypes.c_int64(0)
+        _check(lib().pkv_pool_append_slots(self._h, int(seq), int(n), slots.ctypes.data, copies.ctypes.data, 1,
+                                           ctypes.byref(k)))
+        return slots[:int(n)], copies[:k.value]
+
+    def free_sequence(self, seq: int):
+        _check(lib().pkv_pool_free(self._h, int(seq)))
+
+    def table(self, seq: int):
+        import numpy as np
+        n = lib().pkv_pool_table(self._h, int(seq), None, 0)
+        if n < 0:
+            raise KeyError(seq)
+        out = np.empty(max(n, 1), dtype=np.int32)
+        lib().pkv_pool_table(self._h, int(seq), out.ctypes.data, n)
+        return out[:n].tolist()
+
+    def num_tokens(self, seq: int) -> int:
+        n = lib().pkv_pool_num_tokens(self._h, int(seq))
+        if n < 0:
+            raise KeyError(seq)
+        return int(n)
+
+    def num_free(self) -> int:
+        return int(lib().pkv_pool_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(lib().pkv_pool_refcount(self._h, int(block)))
+
+    def free_list(self):
+        import numpy as np
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        n = lib().pkv_pool_free_list(self._h, out.ctypes.data, self.num_blocks)
+        return out[:n].tolist()
+
+    def build_tables(self, seqs, width: int):
+        """int32 [len(seqs), width] padded tables and int32 [len(seqs)] context lengths."""
+        import numpy as np
+        s = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        tables = np.empty((max(len(s), 1), int(width)), dtype=np.int32)
+        lens = np.empty(max(len(s), 1), dtype=np.int32)
+        _check(lib().pkv_pool_build_tables(self._h, s.ctypes.data, len(s), int(width), tables.ctypes.data,
+                                           lens.ctypes.data))
+        return tables[:len(s)], lens[:len(s)]

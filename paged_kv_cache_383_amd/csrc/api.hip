@@ -17,6 +17,15 @@ namespace {
 
 thread_local std::string g_last_error;
 
+}  // namespace
+
+int pkv::set_error(int code, const std::string& message) {
+  g_last_error = message;
+  return code;
+}
+
+namespace {
+
 int fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -142,6 +151,40 @@ extern "C" int paged_kv_write(const void* k, const void* v, const int64_t* slot_
   hipError_t e = pkv::launch_kv_write(dtype, head_dim, k, v, slot_mapping, num_tokens, k_cache, v_cache,
                                       num_blocks, num_heads, block_size, st);
   if (e != hipSuccess) return hip_fail(e, "paged_kv_write launch");
+  return ok();
+}
+
+extern "C" int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                                    int64_t num_pairs, int64_t num_blocks, int32_t num_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t dtype, void* stream) {
+  if (num_pairs < 0) return fail(PKV_EINVAL, "num_pairs must be >= 0 (got %lld)", (long long)num_pairs);
+  if (int rc = check_shape(dtype, num_heads, head_dim, block_size, num_blocks)) return rc;
+  if (num_pairs == 0) return ok();
+  if (!k_cache || !v_cache || !block_mapping)
+    return fail(PKV_EINVAL, "null pointer among k_cache, v_cache, block_mapping");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    std::vector<int64_t> m(size_t(2 * num_pairs));
+    hipError_t e = hipMemcpyAsync(m.data(), block_mapping, m.size() * sizeof(int64_t), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "PKV_DEBUG copy of block_mapping");
+    std::unordered_set<int64_t> dsts;
+    for (int64_t i = 0; i < num_pairs; ++i) {
+      const int64_t s = m[size_t(2 * i)], d = m[size_t(2 * i + 1)];
+      if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)
+        return fail(PKV_EINVAL, "block_mapping[%lld] = (%lld, %lld) outside [0, %lld)", (long long)i,
+                    (long long)s, (long long)d, (long long)num_blocks);
+      if (!dsts.insert(d).second)
+        return fail(PKV_EINVAL, "block_mapping[%lld] repeats destination %lld", (long long)i, (long long)d);
+    }
+    for (int64_t i = 0; i < num_pairs; ++i)
+      if (dsts.count(m[size_t(2 * i)]))
+        return fail(PKV_EINVAL, "block_mapping[%lld] reads block %lld, which is also a destination",
+                    (long long)i, (long long)m[size_t(2 * i)]);
+  }
+  const int64_t block_bytes = int64_t(num_heads) * block_size * head_dim * elem_bytes(dtype);
+  hipError_t e = pkv::launch_copy_blocks(block_mapping, num_pairs, k_cache, v_cache, num_blocks, block_bytes, st);
+  if (e != hipSuccess) return hip_fail(e, "paged_kv_copy_blocks launch");
   return ok();
 }
 

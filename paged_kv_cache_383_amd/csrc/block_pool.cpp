@@ -1,0 +1,218 @@
+// Host-side block pool: the scheduler's half of paged KV memory management.
+//
+// "PagedAttention" card (llm-engineer.pages.dev), "OS paging과 같은 발상" and
+// "vLLM에서의 위치": the engine decides which physical KV blocks each request
+// gets and appends a block to the request's block table when its cache grows;
+// the GPU worker turns the tables into device tensors.  "vLLM KV cache and
+// PagedAttention explained" (hrletsgo.me): Step 6 (ceil(n / 16) blocks at
+// prefill, a new block at each block boundary during decode), Step 7 (a
+// finished request's blocks return to the pool, immediately reusable), Step 9
+// (blocks of a shared prefix carry a reference count; a write into a shared
+// block first copies it into a new block that only the writer's table uses).
+//
+// Policy (the pages leave these open):
+//   * token t of a sequence lives in logical block t / block_size;
+//   * a block is copied only while another table still holds it (count > 1);
+//     the last holder writes in place;
+//   * allocation takes blocks from the front of an ordered free list, and the
+//     blocks a free releases go back to the front in table order, so the next
+//     request receives exactly the space just released;
+//   * every operation is all-or-nothing: on PKV_ENOSPACE nothing changes.
+#include <deque>
+#include <new>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "pagedkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+int pool_fail(int code, const std::string& msg) { return pkv::set_error(code, msg); }
+
+struct Sequence {
+  std::vector<int32_t> table;
+  int64_t tokens = 0;
+};
+
+}  // namespace
+
+struct pkv_block_pool {
+  int64_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::deque<int32_t> free_list;          // front = next block handed out
+  std::vector<int32_t> refcount;          // tables holding each block
+  std::unordered_map<int64_t, Sequence> seqs;
+
+  int64_t blocks_for(int64_t tokens) const { return (tokens + block_size - 1) / block_size; }
+
+  int32_t take() {
+    const int32_t b = free_list.front();
+    free_list.pop_front();
+    refcount[b] = 1;
+    return b;
+  }
+};
+
+extern "C" pkv_block_pool* pkv_pool_create(int64_t num_blocks, int32_t block_size, const int32_t* free_order) {
+  if (num_blocks <= 0 || num_blocks > INT32_MAX || block_size <= 0) {
+    pool_fail(PKV_EINVAL, "num_blocks must be in [1, 2^31) and block_size positive");
+    return nullptr;
+  }
+  pkv_block_pool* p = new (std::nothrow) pkv_block_pool;
+  if (!p) {
+    pool_fail(PKV_EINVAL, "out of host memory");
+    return nullptr;
+  }
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->refcount.assign(size_t(num_blocks), 0);
+  if (free_order) {
+    std::vector<char> seen(size_t(num_blocks), 0);
+    for (int64_t i = 0; i < num_blocks; ++i) {
+      const int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[size_t(b)]) {
+        delete p;
+        pool_fail(PKV_EINVAL, "free_order must list every block id in [0, num_blocks) exactly once");
+        return nullptr;
+      }
+      seen[size_t(b)] = 1;
+      p->free_list.push_back(b);
+    }
+  } else {
+    for (int64_t b = 0; b < num_blocks; ++b) p->free_list.push_back(int32_t(b));
+  }
+  pkv::set_error(PKV_OK, "");
+  return p;
+}
+
+extern "C" void pkv_pool_destroy(pkv_block_pool* p) { delete p; }
+
+extern "C" int pkv_pool_allocate(pkv_block_pool* p, int64_t seq, int64_t num_tokens) {
+  if (!p || num_tokens < 0) return pool_fail(PKV_EINVAL, "null pool or negative token count");
+  if (p->seqs.count(seq)) return pool_fail(PKV_EINVAL, "sequence " + std::to_string(seq) + " already exists");
+  const int64_t need = p->blocks_for(num_tokens);
+  if (need > int64_t(p->free_list.size()))
+    return pool_fail(PKV_ENOSPACE, std::to_string(need) + " blocks needed, " +
+                                       std::to_string(p->free_list.size()) + " free");
+  Sequence s;
+  s.tokens = num_tokens;
+  s.table.reserve(size_t(need));
+  for (int64_t i = 0; i < need; ++i) s.table.push_back(p->take());
+  p->seqs.emplace(seq, std::move(s));
+  return pkv::set_error(PKV_OK, "");
+}
+
+extern "C" int pkv_pool_fork(pkv_block_pool* p, int64_t parent, int64_t child) {
+  if (!p) return pool_fail(PKV_EINVAL, "null pool");
+  auto it = p->seqs.find(parent);
+  if (it == p->seqs.end()) return pool_fail(PKV_EINVAL, "unknown sequence " + std::to_string(parent));
+  if (p->seqs.count(child)) return pool_fail(PKV_EINVAL, "sequence " + std::to_string(child) + " already exists");
+  Sequence s = it->second;
+  for (int32_t b : s.table) ++p->refcount[size_t(b)];
+  p->seqs.emplace(child, std::move(s));
+  return pkv::set_error(PKV_OK, "");
+}
+
+extern "C" int pkv_pool_append_slots(pkv_block_pool* p, int64_t seq, int64_t n, int64_t* slots_out,
+                                     int64_t* copies_out, int64_t max_copies, int64_t* num_copies) {
+  if (!p || n < 0 || (n > 0 && !slots_out) || !num_copies)
+    return pool_fail(PKV_EINVAL, "null pool, output pointer or negative count");
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return pool_fail(PKV_EINVAL, "unknown sequence " + std::to_string(seq));
+  Sequence& s = it->second;
+  const int64_t bs = p->block_size;
+  // Blocks this call needs: one per boundary crossed, plus a private copy of
+  // the partly filled last block when another table still holds it.
+  int64_t need = p->blocks_for(s.tokens + n) - int64_t(s.table.size());
+  const bool cow = n > 0 && s.tokens % bs != 0 && p->refcount[size_t(s.table.back())] > 1;
+  if (cow) {
+    ++need;
+    if (max_copies < 1 || !copies_out) return pool_fail(PKV_EINVAL, "room for one block copy is needed");
+  }
+  if (need > int64_t(p->free_list.size()))
+    return pool_fail(PKV_ENOSPACE, std::to_string(need) + " blocks needed, " +
+                                       std::to_string(p->free_list.size()) + " free");
+  *num_copies = 0;
+  for (int64_t t = s.tokens; t < s.tokens + n; ++t) {
+    const int64_t j = t / bs, off = t % bs;
+    if (j == int64_t(s.table.size())) {
+      s.table.push_back(p->take());
+    } else if (p->refcount[size_t(s.table[size_t(j)])] > 1) {
+      const int32_t src = s.table[size_t(j)];
+      const int32_t dst = p->take();
+      --p->refcount[size_t(src)];
+      s.table[size_t(j)] = dst;
+      copies_out[2 * *num_copies] = src;
+      copies_out[2 * *num_copies + 1] = dst;
+      ++*num_copies;
+    }
+    slots_out[t - s.tokens] = int64_t(s.table[size_t(j)]) * bs + off;
+  }
+  s.tokens += n;
+  return pkv::set_error(PKV_OK, "");
+}
+
+extern "C" int pkv_pool_free(pkv_block_pool* p, int64_t seq) {
+  if (!p) return pool_fail(PKV_EINVAL, "null pool");
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return pool_fail(PKV_EINVAL, "unknown sequence " + std::to_string(seq));
+  const std::vector<int32_t>& t = it->second.table;
+  for (auto b = t.rbegin(); b != t.rend(); ++b)       // pushed in reverse: the front keeps table order
+    if (--p->refcount[size_t(*b)] == 0) p->free_list.push_front(*b);
+  p->seqs.erase(it);
+  return pkv::set_error(PKV_OK, "");
+}
+
+extern "C" int64_t pkv_pool_num_free(const pkv_block_pool* p) { return p ? int64_t(p->free_list.size()) : -1; }
+
+extern "C" int32_t pkv_pool_refcount(const pkv_block_pool* p, int64_t block) {
+  if (!p || block < 0 || block >= p->num_blocks) return -1;
+  return p->refcount[size_t(block)];
+}
+
+extern "C" int64_t pkv_pool_num_tokens(const pkv_block_pool* p, int64_t seq) {
+  if (!p) return -1;
+  auto it = p->seqs.find(seq);
+  return it == p->seqs.end() ? -1 : it->second.tokens;
+}
+
+extern "C" int64_t pkv_pool_table(const pkv_block_pool* p, int64_t seq, int32_t* out, int64_t cap) {
+  if (!p) return -1;
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return -1;
+  const std::vector<int32_t>& t = it->second.table;
+  for (int64_t i = 0; i < int64_t(t.size()) && i < cap; ++i) out[i] = t[size_t(i)];
+  return int64_t(t.size());
+}
+
+extern "C" int64_t pkv_pool_free_list(const pkv_block_pool* p, int32_t* out, int64_t cap) {
+  if (!p) return -1;
+  int64_t i = 0;
+  for (auto it = p->free_list.begin(); it != p->free_list.end() && i < cap; ++it) out[i++] = *it;
+  return int64_t(p->free_list.size());
+}
+
+extern "C" int pkv_pool_build_tables(const pkv_block_pool* p, const int64_t* seqs, int32_t n, int32_t width,
+                                     int32_t* tables_out, int32_t* lens_out) {
+  if (!p || n < 0 || width <= 0 || (n > 0 && (!seqs || !tables_out || !lens_out)))
+    return pool_fail(PKV_EINVAL, "null pool or output, or non-positive width");
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = p->seqs.find(seqs[i]);
+    if (it == p->seqs.end()) return pool_fail(PKV_EINVAL, "unknown sequence " + std::to_string(seqs[i]));
+    const Sequence& s = it->second;
+    if (int64_t(s.table.size()) > width)
+      return pool_fail(PKV_EINVAL, "sequence " + std::to_string(seqs[i]) + " holds " +
+                                       std::to_string(s.table.size()) + " blocks, wider than " +
+                                       std::to_string(width));
+    if (s.tokens > INT32_MAX) return pool_fail(PKV_EINVAL, "context length exceeds int32");
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const Sequence& s = p->seqs.find(seqs[i])->second;
+    int32_t* row = tables_out + int64_t(i) * width;
+    for (int32_t j = 0; j < width; ++j) row[j] = j < int32_t(s.table.size()) ? s.table[size_t(j)] : -1;
+    lens_out[i] = int32_t(s.tokens);
+  }
+  return pkv::set_error(PKV_OK, "");
+}

@@ -7,7 +7,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace pkv {
+
+// Records the calling thread's last status text (read by pkv_last_error) and
+// returns `code`.
+int set_error(int code, const std::string& message);
 
 // Split-context workspace: three fp32 arrays, each 256-byte aligned.
 //   m    [num_seqs, num_heads, P]      running max of a partition (base-2 logits)
@@ -57,5 +63,8 @@ hipError_t launch_kv_write(int dtype, int head_dim, const void* k, const void* v
                            const int64_t* slot_mapping, int64_t num_tokens, void* k_cache,
                            void* v_cache, int64_t num_blocks, int32_t num_heads,
                            int32_t block_size, hipStream_t stream);
+
+hipError_t launch_copy_blocks(const int64_t* block_mapping, int64_t num_pairs, void* k_cache, void* v_cache,
+                              int64_t num_blocks, int64_t block_bytes, hipStream_t stream);
 
 }  // namespace pkv

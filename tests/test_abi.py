@@ -34,7 +34,9 @@ def declared_functions():
 def test_header_declares_the_two_calls():
     fns = declared_functions()
     assert {"paged_kv_write", "paged_attention_decode", "paged_attention_workspace_bytes",
-            "paged_attention_partition_size", "pkv_last_error"} <= set(fns)
+            "paged_attention_partition_size", "paged_kv_copy_blocks", "pkv_last_error", "pkv_pool_create",
+            "pkv_pool_allocate", "pkv_pool_fork", "pkv_pool_append_slots", "pkv_pool_free",
+            "pkv_pool_build_tables"} <= set(fns)
 
 
 def test_library_exports_every_declared_function(libpath):
@@ -54,6 +56,11 @@ vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_siz
 lib.paged_kv_write.argtypes = [vp, vp, vp, i64, vp, vp, i64, i32, i32, i32, i32, vp]
 lib.paged_attention_decode.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i64,
                                        ctypes.c_float, i32, vp, vp, sz, i32, vp]
+lib.paged_kv_copy_blocks.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, vp]
+def cp(**kw):
+    a = dict(k=F, v=F, m=F, n=3, NB=64, H=4, D=64, bs=16, dt=0)
+    a.update(kw)
+    return lib.paged_kv_copy_blocks(a["k"], a["v"], a["m"], a["n"], a["NB"], a["H"], a["D"], a["bs"], a["dt"], None)
 lib.paged_attention_workspace_bytes.argtypes = [i32] * 6
 lib.paged_attention_workspace_bytes.restype = sz
 lib.pkv_last_error.restype = ctypes.c_char_p
@@ -84,6 +91,8 @@ cases = [
   ("wr_dtype", lambda: wr(dt=3), 2), ("wr_null", lambda: wr(s=None), 1),
   ("wr_neg_tokens", lambda: wr(T=-1), 1), ("wr_zero_tokens", lambda: wr(T=0, k=None), 0),
   ("wr_head_dim", lambda: wr(D=80), 2), ("wr_block", lambda: wr(bs=64), 2),
+  ("cp_neg", lambda: cp(n=-1), 1), ("cp_null", lambda: cp(m=None), 1), ("cp_zero", lambda: cp(n=0, k=None), 0),
+  ("cp_dtype", lambda: cp(dt=9), 2), ("cp_blocks", lambda: cp(NB=0), 1),
 ]
 for name, call, want in cases:
     got = call()

@@ -1,0 +1,179 @@
+"""The library's C++ block pool (pkv_pool_*) against the oracle's block pool.
+
+Runs on the CPU: the pool is host code and touches no GPU memory.  Two checks:
+the oracle's pool pins (the pages' block-42, prefix-sharing and parallel-sampling
+examples, invariants, data-level contents) run unchanged on an adapter over the
+C++ pool, and random operation sequences drive both pools in lockstep, comparing
+tables, token counts, slots, copy pairs, reference counts and free-list order
+after every operation.
+"""
+import types
+
+import numpy as np
+import pytest
+
+import oracle.block_manager as BM
+import oracle.oracle as O
+import oracle_pins as P
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    from paged_kv_cache_383_amd import build as b
+    import os
+    if not os.path.exists(b.LIB_PATH):
+        b.build()
+    import paged_kv_cache_383_amd as m
+    m.lib()
+    return m
+
+
+class _Adapter:
+    """The oracle pool's interface over the C++ pool (for the pins)."""
+
+    def __init__(self, pkv, num_blocks, block_size, free_order=None):
+        self.p = pkv.BlockPool(num_blocks, block_size, free_order)
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self._ids = {}                         # the pins name sequences by any hashable; the pool by int64
+        self._next = 0
+
+    def _id(self, seq):
+        if seq not in self._ids:
+            self._ids[seq] = self._next
+            self._next += 1
+        return self._ids[seq]
+
+    def allocate(self, seq, n):
+        t = self.p.allocate(self._next, n)     # registered only once the pool has it
+        self._id(seq)
+        return t
+
+    def fork(self, parent, child):
+        self.p.fork(self._id(parent), self._next)
+        self._id(child)
+
+    def append_slots(self, seq, n):
+        slots, copies = self.p.append_slots(self._id(seq), n)
+        return [int(x) for x in slots], [(int(a), int(b)) for a, b in copies]
+
+    def free_sequence(self, seq):
+        before = set(self.p.free_list())
+        self.p.free_sequence(self._id(seq))
+        self._ids.pop(seq)
+        return [b for b in self.p.free_list() if b not in before]
+
+    def table(self, seq):
+        return self.p.table(self._id(seq))
+
+    def num_free(self):
+        return self.p.num_free()
+
+    @property
+    def refcount(self):
+        return [self.p.refcount(b) for b in range(self.num_blocks)]
+
+    @property
+    def tables(self):
+        return {s: self.p.table(i) for s, i in self._ids.items()}
+
+    @property
+    def tokens(self):
+        return {s: self.p.num_tokens(i) for s, i in self._ids.items()}
+
+    @property
+    def free(self):
+        return self.p.free_list()
+
+
+def _adapter_module(pkv):
+    m = types.SimpleNamespace()
+    m.BlockPool = lambda nb, bs, free_order=None: _Adapter(pkv, nb, bs, free_order)
+    m.OutOfBlocks = pkv.OutOfBlocks
+    m.copy_blocks = BM.copy_blocks
+    return m
+
+
+@pytest.mark.parametrize("pin", P.POOL_PINS, ids=lambda f: f.__name__)
+def test_pool_pins_hold_for_the_library_pool(pkv, pin):
+    pin(_adapter_module(pkv), O)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_library_pool_matches_oracle_pool(pkv, seed):
+    rng = np.random.default_rng(100 + seed)
+    NB, bs = int(rng.integers(8, 80)), int(rng.choice([16, 32]))
+    order = rng.permutation(NB)
+    ref = BM.BlockPool(NB, bs, order)
+    lib = pkv.BlockPool(NB, bs, order)
+    live, next_id = [], 0
+    for step in range(500):
+        r = rng.random()
+        op = ("alloc" if r < 0.25 or not live else "fork" if r < 0.4 else "append" if r < 0.85 else "free")
+        if op == "alloc":
+            n = int(rng.integers(0, 4 * bs))
+            try:
+                ref.allocate(next_id, n)
+                ok = True
+            except BM.OutOfBlocks:
+                ok = False
+            if ok:
+                lib.allocate(next_id, n)
+                live.append(next_id)
+                next_id += 1
+            else:
+                with pytest.raises(pkv.OutOfBlocks):
+                    lib.allocate(next_id, n)
+        elif op == "fork":
+            parent = live[int(rng.integers(len(live)))]
+            ref.fork(parent, next_id)
+            lib.fork(parent, next_id)
+            live.append(next_id)
+            next_id += 1
+        elif op == "append":
+            s = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(0, 2 * bs))
+            try:
+                want = ref.append_slots(s, n)
+            except BM.OutOfBlocks:
+                want = None
+            if want is None:
+                with pytest.raises(pkv.OutOfBlocks):
+                    lib.append_slots(s, n)
+            else:
+                slots, copies = lib.append_slots(s, n)
+                assert slots.tolist() == want[0], (step, s)
+                assert [tuple(c) for c in copies.tolist()] == want[1], (step, s)
+        else:
+            s = live.pop(int(rng.integers(len(live))))
+            ref.free_sequence(s)
+            lib.free_sequence(s)
+        assert lib.free_list() == ref.free, step
+        assert [lib.refcount(b) for b in range(NB)] == ref.refcount, step
+        for s in live:
+            assert lib.table(s) == ref.table(s) and lib.num_tokens(s) == ref.tokens[s]
+    if live:
+        t_lib, l_lib = lib.build_tables(live, 4 * bs + 8)
+        t_ref, l_ref = ref.padded_tables(live, 4 * bs + 8)
+        assert np.array_equal(t_lib, t_ref) and np.array_equal(l_lib, l_ref)
+
+
+def test_errors_leave_the_pool_unchanged(pkv):
+    p = pkv.BlockPool(4, 16)
+    p.allocate(1, 40)                          # 3 blocks
+    p.fork(1, 2)
+    before = (p.free_list(), p.table(1), p.table(2), [p.refcount(b) for b in range(4)])
+    with pytest.raises(pkv.OutOfBlocks):
+        p.append_slots(2, 30)                  # needs a copy of the shared last block + 1 new block
+    with pytest.raises(pkv.OutOfBlocks):
+        p.allocate(3, 17)
+    with pytest.raises(pkv.PagedKVError, match="unknown sequence"):
+        p.append_slots(9, 1)
+    with pytest.raises(pkv.PagedKVError, match="already exists"):
+        p.fork(1, 2)
+    with pytest.raises(pkv.PagedKVError, match="unknown sequence"):
+        p.free_sequence(7)
+    with pytest.raises(pkv.PagedKVError, match="wider"):
+        p.build_tables([1], 2)
+    assert before == (p.free_list(), p.table(1), p.table(2), [p.refcount(b) for b in range(4)])
+    with pytest.raises(pkv.PagedKVError, match="exactly once"):
+        pkv.BlockPool(3, 16, [0, 0, 1])

@@ -265,3 +265,35 @@ def storage_numpy(t):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+# ---------------------------------------------------------------- parallel sampling over shared prompts
+
+@dataclass(frozen=True)
+class SamplingConfig:
+    """Parallel sampling ("vLLM KV cache and PagedAttention explained", Step 9): each prompt's
+    blocks are shared by ``samples`` sequences, at the LLaMA-2-13B layer shape."""
+    name: str = "parallel_sampling_16x4_llama2_13b_layer_ctx128-2048_bf16"
+    prompts: int = 16
+    samples: int = 4
+    num_heads: int = 40
+    head_dim: int = 128
+    block_size: int = 16
+    dtype: str = BF16
+    min_len: int = 128
+    max_len: int = 2048
+    seed: int = SEED_BASE + 100
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+def sampling_prompts(cfg: SamplingConfig, seed: int | None = None):
+    """Prompt lengths, pool size (1.25x the prompts' blocks plus one block per sample for copies and
+    growth) and a shuffled free order."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    lens = rng.integers(cfg.min_len, cfg.max_len + 1, cfg.prompts)
+    needed = int(((lens + cfg.block_size - 1) // cfg.block_size).sum())
+    nb = ceil_div(5 * needed, 4) + cfg.prompts * cfg.samples
+    return lens.astype(np.int64), nb, rng.permutation(nb).astype(np.int32)
