@@ -92,6 +92,22 @@ def kv_write(k, v, slot_mapping, k_cache, v_cache, block_size: int):
     return k_out, v_out
 
 
+def newest_token_slots(block_tables, context_lens, block_size: int) -> np.ndarray:
+    """Flat slot of each sequence's newest token (position L - 1), or -1 for an empty row.
+
+    This is where a decode step writes the token it adds ([explain] Step 6:
+    the decode token's K/V goes to the next slot of the sequence's block, a
+    new block once the previous one is full): logical block (L - 1) // bs,
+    offset (L - 1) % bs, through the block table.
+    """
+    out = np.full(len(context_lens), -1, dtype=np.int64)
+    for i, L in enumerate(np.asarray(context_lens).tolist()):
+        if L > 0:
+            b = int(block_tables[i][(L - 1) // block_size])
+            out[i] = b * block_size + (L - 1) % block_size
+    return out
+
+
 def gather_sequence(cache, table_row, num_tokens: int, block_size: int, dtype: str) -> np.ndarray:
     """Logical float64 [H, L, D] K (or V) of one sequence, read through its table.
 

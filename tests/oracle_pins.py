@@ -391,10 +391,28 @@ def pin_prefix_sharing(o):
     assert np.array_equal(a, b)
 
 
+def pin_newest_token_slots(o):
+    """The pages' block 42: after the 6-token prompt and one decode token the newest token (the 7th)
+    sits in slot 6 (flat 678); the 16th fills slot 15; the 17th opens the table's second block."""
+    g = golden("slot_example.json")
+    bs = g["block_size"]
+    tables = np.array([[42, 9], [42, 9], [42, 9], [5, -1], [42, 9]], dtype=np.int32)
+    lens = np.array([7, 16, 17, 0, 1])
+    got = o.newest_token_slots(tables, lens, bs).tolist()
+    assert got == [g["decode_flat_slot"], 42 * bs + 15, 9 * bs, -1, 42 * bs]
+    # agrees with where a write of the newest token makes the gather find it
+    rng = np.random.default_rng(24)
+    c = Case(rng, [3, 16, 17, 40], H=2, D=4, bs=bs)
+    s = o.newest_token_slots(c.tables, c.context_lens, bs)
+    for i, L in enumerate(c.lens):
+        b, off = o.slot_to_block_offset(int(s[i]), bs)
+        assert np.array_equal(c.k_pool[b, :, off, :], c.Klog[i][L - 1])
+
+
 PINS = [pin_block_counts, pin_storage_upcast, pin_round_to_storage, pin_slot_example,
         pin_write_then_read, pin_write_bitwise, pin_brute_force, pin_pages_tables,
         pin_permutation_invariance, pin_poison_invariance, pin_closed_forms,
-        pin_split_equals_single, pin_prefix_sharing]
+        pin_split_equals_single, pin_prefix_sharing, pin_newest_token_slots]
 
 
 # ---------------------------------------------------------------- block pool pins

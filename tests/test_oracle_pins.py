@@ -127,7 +127,22 @@ def _write_ignores_padding(k, v, slot_mapping, k_cache, v_cache, block_size):
     return k_out, v_out
 
 
+def _slots_oldest_token(block_tables, context_lens, block_size):
+    lens = np.where(np.asarray(context_lens) > 0, np.minimum(np.asarray(context_lens), 2), 0)
+    return O.__dict__["_orig_newest_token_slots"](block_tables, lens, block_size)
+
+
+def _slots_position_l(block_tables, context_lens, block_size):
+    out = np.full(len(context_lens), -1, dtype=np.int64)
+    for i, L in enumerate(np.asarray(context_lens).tolist()):
+        if L > 0:
+            out[i] = int(block_tables[i][L // block_size]) * block_size + L % block_size
+    return out
+
+
 MUTANTS = {
+    "newest slot taken at position 1": ("newest_token_slots", _slots_oldest_token),
+    "newest slot taken at position L": ("newest_token_slots", _slots_position_l),
     "blocks_needed floors": ("blocks_needed", _floor_blocks),
     "gather drops the head transpose": ("gather_sequence", _gather_no_transpose),
     "gather reads the next table entry": ("gather_sequence", _gather_shifted_table),
