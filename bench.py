@@ -279,15 +279,136 @@ def parallel_sampling(args):
     print(json.dumps(rec), flush=True)
 
 
+def continuous_batching(args):
+    """A multi-step decode loop: rows run requests from a seeded stream; each step the C++ block pool and
+    batch planner reserve every running row's slot, and the prompt writes of new requests,
+    paged_kv_prepare_step, block copies, paged_kv_write and paged_attention_decode run on the GPU; a
+    request that reaches its length releases its blocks and its row takes the next request."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_383_amd.decode_loop import DecodeLoop
+    cfg = W.BatchingConfig()
+    dev = torch.device("cuda:0")
+    H, D, bs, R = cfg.num_heads, cfg.head_dim, cfg.block_size, cfg.rows
+    es = elem_bytes(cfg.dtype)
+    dt = W.torch_dtype(cfg.dtype)
+    NB = R * cfg.width                         # every row can reach its longest request: no preemption
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    kc = torch.empty((NB, H, bs, D), dtype=dt, device=dev)
+    vc = torch.empty_like(kc)
+    W._randn_into(kc, gen, 1.0, 512)
+    W._randn_into(vc, gen, 1.0, 512)
+    src_k = torch.randn((cfg.prompt_max, H, D), generator=gen, device=dev).to(dt)
+    src_v = torch.randn((cfg.prompt_max, H, D), generator=gen, device=dev).to(dt)
+    q = torch.randn((R, H, D), generator=gen, device=dev).to(dt)
+    kn = torch.randn((R, H, D), generator=gen, device=dev).to(dt)
+    vn = torch.randn((R, H, D), generator=gen, device=dev).to(dt)
+    out = torch.empty_like(q)
+    n_req = 20000
+    prompts, gens = W.batching_requests(cfg, n_req)
+    loop = DecodeLoop(kc, vc, R, cfg.width, free_order=np.random.default_rng(cfg.seed).permutation(NB))
+    state = {"next": 0, "row_req": [-1] * R, "left": [0] * R}
+
+    def fill():
+        for r in range(R):
+            if state["row_req"][r] < 0 and state["next"] < n_req:
+                i = state["next"]
+                P = int(prompts[i])
+                loop.admit(r, i, src_k[:P], src_v[:P])
+                state["row_req"][r], state["left"][r] = i, int(gens[i])
+                state["next"] += 1
+
+    def end_of_step():
+        for r in range(R):
+            if state["row_req"][r] >= 0:
+                state["left"][r] -= 1
+                if state["left"][r] == 0:
+                    loop.release(r)
+                    state["row_req"][r] = -1
+
+    totals = {"kv": 0, "tokens": 0, "prompt": 0, "copies": 0, "rows": 0}
+
+    def one_step(count):
+        fill()
+        loop.step(q, kn, vn, out=out)
+        if count:
+            lens = loop.last_lens.astype(np.int64)
+            totals["kv"] += int(lens.sum())
+            totals["rows"] += int((lens > 0).sum())
+            totals["prompt"] += loop.last_prompt_tokens
+            totals["copies"] += len(loop.last_copies)
+        end_of_step()
+
+    log(f"{cfg.name}: pool {NB} blocks ({2 * NB * H * bs * D * es / 1e9:.1f} GB K+V), {R} rows")
+    for _ in range(args.warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(args.steps):
+        one_step(True)
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = a.elapsed_time(b) * 1e-3
+    row_b = H * D * es
+    nbytes = (totals["kv"] * 2 * row_b + totals["rows"] * 2 * row_b       # decode: K/V reads, q + out
+              + totals["rows"] * 4 * row_b + totals["prompt"] * 4 * row_b  # new-token and prompt writes
+              + totals["copies"] * 4 * bs * row_b)                         # copy-on-write
+    # the decode kernel alone at the loop's final state, back to back
+    lens_now = loop.last_lens.astype(np.int64)
+    ctx = lens_now[lens_now > 0]
+    decode_b = int(ctx.sum()) * 2 * row_b + len(ctx) * 2 * row_b + 4 * int(((ctx + bs - 1) // bs).sum()) + 4 * R
+    from paged_kv_cache_383_amd import paged_attention_decode
+    for _ in range(3):
+        paged_attention_decode(q, kc, vc, loop.tables, loop.lens, loop.scale, out=out, workspace=loop.workspace)
+    a.record()
+    for _ in range(20):
+        paged_attention_decode(q, kc, vc, loop.tables, loop.lens, loop.scale, out=out, workspace=loop.workspace)
+    b.record()
+    torch.cuda.synchronize()
+    decode_us = a.elapsed_time(b) * 1e3 / 20
+    achieved = decode_b / decode_us / 1e3
+    step_s = wall / args.steps
+    log(f"{args.steps} steps in {wall * 1e3:.1f} ms (GPU {gpu_s * 1e3:.1f} ms): {step_s * 1e6:.1f} us/step, "
+        f"{totals['rows'] / wall:.0f} generated tokens/s, {nbytes / wall / 1e9:.0f} GB/s; "
+        f"{state['next']} requests admitted; decode alone {decode_us:.1f} us = {achieved:.0f} GB/s")
+    rec = {
+        "metric": METRIC, "value": round(nbytes / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "rows": R, "num_heads": H, "head_dim": D, "block_size": bs,
+                   "pool_blocks": NB, "requests_admitted": state["next"],
+                   "step": "plan (host) + prompt writes + paged_kv_prepare_step + paged_kv_copy_blocks + "
+                           "paged_kv_write + paged_attention_decode",
+                   "algorithmic_bytes": nbytes},
+        "tokens_heads_per_s": round(totals["kv"] * H / wall, 1),
+        "generated_tokens_per_s": round(totals["rows"] / wall, 1),
+        "mean_running_rows": round(totals["rows"] / args.steps, 1),
+        "gpu_time_fraction": round(gpu_s / wall, 4),
+        "roofline": {"kernel": "paged_attention_decode (decode_partition_kernel), loop's final batch",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": decode_b, "mean_launch_us": round(decode_us, 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--workload", choices=["decode", "parallel_sampling"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "parallel_sampling", "continuous_batching"], default="decode",
                     help="decode: one decode step of --config; parallel_sampling: a decode step over "
-                         "prompts shared by parallel samples (copy-on-write copies + write + decode)")
+                         "prompts shared by parallel samples (copy-on-write copies + write + decode); "
+                         "continuous_batching: a many-step decode loop with admissions and releases")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="split-context partition in tokens (0 = one pass); default: the library's choice")
     ap.add_argument("--rotate", type=int, default=None, help="independent input copies cycled over")
@@ -314,6 +435,9 @@ def main():
     pkv.lib()
     if args.workload == "parallel_sampling":
         parallel_sampling(args)
+        return
+    if args.workload == "continuous_batching":
+        continuous_batching(args)
         return
 
     dev = torch.device("cuda:0")

@@ -177,6 +177,29 @@ int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
                          int64_t num_blocks, int32_t num_heads, int32_t head_dim, int32_t block_size,
                          int32_t dtype, void* stream);
 
+/*
+ * paged_kv_prepare_step -- a decode step's metadata, updated on the device.
+ * Applies table updates, sets context lengths, and writes each row's slot
+ * mapping: the slot of its newest token, block_tables[r, (L-1) / block_size] *
+ * block_size + (L-1) % block_size with L = context_lens[r] ([explain] Step 6:
+ * the decode token goes to the next slot of the sequence's last block), or -1
+ * for an idle row (L = 0), which paged_kv_write then skips.  pkv_batch_plan_step
+ * produces the updates and lengths.
+ *
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32, device, updated in place
+ *   context_lens  [num_seqs] int32, device, overwritten with new_lens when given
+ *   updates       [num_updates, 3] int32 (row, column, block id), device; the
+ *                 (row, column) pairs of one call are distinct
+ *   new_lens      [num_seqs] int32, device, or NULL to keep context_lens
+ *   slot_mapping  [num_seqs] int64, device, written (NULL: not computed)
+ * All device pointers; the call is asynchronous on `stream`.  Entries outside
+ * the arrays are skipped; a row whose length or block id is out of range gets
+ * slot -1.  Returns PKV_OK, or an error status with nothing launched.
+ */
+int paged_kv_prepare_step(int32_t* block_tables, int32_t max_blocks_per_seq, int32_t* context_lens, int32_t num_seqs,
+                          const int32_t* updates, int64_t num_updates, const int32_t* new_lens,
+                          int64_t* slot_mapping, int32_t block_size, int64_t num_blocks, void* stream);
+
 /* Text of the calling thread's last non-OK status (empty string if none). */
 const char* pkv_last_error(void);
 
@@ -242,6 +265,41 @@ int32_t pkv_pool_refcount(const pkv_block_pool* pool, int64_t block);
 int64_t pkv_pool_num_tokens(const pkv_block_pool* pool, int64_t seq);
 int64_t pkv_pool_table(const pkv_block_pool* pool, int64_t seq, int32_t* out, int64_t cap);
 int64_t pkv_pool_free_list(const pkv_block_pool* pool, int32_t* out, int64_t cap);
+
+/*
+ * ---- Batch: decode rows over a pool, with a mirror of the device tables ----
+ *
+ * A batch of `rows` rows (each idle or running one sequence of `pool`) whose
+ * block tables live on the device as [rows, width] int32, filled with -1 before
+ * the first step.  The batch keeps a host mirror of them, so a plan lists only
+ * the entries that changed since the previous plan: a new block every
+ * block_size tokens, a copy-on-write replacement, a reassigned row.  It is the
+ * bookkeeping of a continuous-batching loop ([explain] Step 8: a finished
+ * request's row is immediately given to a new one; the policy of which request
+ * comes next is the caller's).  Host pointers; not thread-safe.  The batch
+ * borrows the pool, which must outlive it.
+ */
+typedef struct pkv_batch pkv_batch;
+
+pkv_batch* pkv_batch_create(pkv_block_pool* pool, int32_t rows, int32_t width);
+void pkv_batch_destroy(pkv_batch* batch);
+
+/* Row `row` now runs sequence `seq` (which must exist in the pool and fit in
+ * `width` blocks), or is idle when seq < 0.  Takes effect at the next plan. */
+int pkv_batch_set_row(pkv_batch* batch, int32_t row, int64_t seq);
+
+/* One step's bookkeeping.  Every non-idle row's sequence grows by
+ * tokens_per_row tokens (pkv_pool_append_slots; 1 for a decode step, 0 to only
+ * synchronise the tables).  Outputs: updates_out [n_updates, 3] (row, column,
+ * block id; -1 clears an entry), which must hold rows * width entries;
+ * lens_out [rows], every row's context length after the step (0 when idle);
+ * copies_out [n_copies, 2], the block copies to run before the step's writes.
+ * Upload updates and lens, then paged_kv_prepare_step, paged_kv_copy_blocks,
+ * paged_kv_write and paged_attention_decode.  PKV_ENOSPACE (too few free
+ * blocks) and PKV_EINVAL leave the pool and the batch unchanged. */
+int pkv_batch_plan_step(pkv_batch* batch, int32_t tokens_per_row, int32_t* updates_out, int64_t max_updates,
+                        int64_t* n_updates, int32_t* lens_out, int64_t* copies_out, int64_t max_copies,
+                        int64_t* n_copies);
 
 #ifdef __cplusplus
 }

@@ -75,6 +75,10 @@ def lib() -> ctypes.CDLL:
             "pkv_pool_num_free": ([vp], i64), "pkv_pool_refcount": ([vp, i64], i32),
             "pkv_pool_num_tokens": ([vp, i64], i64), "pkv_pool_table": ([vp, i64, vp, i64], i64),
             "pkv_pool_free_list": ([vp, vp, i64], i64),
+            "pkv_batch_create": ([vp, i32, i32], vp), "pkv_batch_destroy": ([vp], None),
+            "pkv_batch_set_row": ([vp, i32, i64], ctypes.c_int),
+            "pkv_batch_plan_step": ([vp, i32, vp, i64, vp, vp, vp, i64, vp], ctypes.c_int),
+            "paged_kv_prepare_step": ([vp, i32, vp, i32, vp, i64, vp, vp, i32, i64, vp], ctypes.c_int),
         }
         for name, (args, res) in pool_fns.items():
             getattr(L, name).argtypes = args
@@ -282,3 +286,59 @@ class BlockPool:
         _check(lib().pkv_pool_build_tables(self._h, s.ctypes.data, len(s), int(width), tables.ctypes.data,
                                            lens.ctypes.data))
         return tables[:len(s)], lens[:len(s)]
+
+
+def paged_kv_prepare_step(block_tables, context_lens, updates, new_lens, slot_mapping, block_size, num_blocks):
+    """Apply (row, column, block) table updates and new lengths on the device; write each row's newest-token
+    slot into slot_mapping (int64 [rows]; -1 for idle rows).  ``updates`` int32 [n, 3] or None;
+    ``new_lens`` int32 [rows] or None."""
+    import torch
+    _device_tensor("block_tables", block_tables, torch.int32, 2)
+    _device_tensor("context_lens", context_lens, torch.int32, 1)
+    rows, width = block_tables.shape
+    n = 0
+    if updates is not None:
+        _device_tensor("updates", updates, torch.int32, 2)
+        n = updates.shape[0]
+    if new_lens is not None:
+        _device_tensor("new_lens", new_lens, torch.int32, 1)
+    if slot_mapping is not None:
+        _device_tensor("slot_mapping", slot_mapping, torch.int64, 1)
+    with torch.cuda.device(block_tables.device):
+        _check(lib().paged_kv_prepare_step(block_tables.data_ptr(), width, context_lens.data_ptr(), rows,
+                                           None if updates is None else updates.data_ptr(), n,
+                                           None if new_lens is None else new_lens.data_ptr(),
+                                           None if slot_mapping is None else slot_mapping.data_ptr(),
+                                           int(block_size), int(num_blocks), _stream(block_tables.device)))
+
+
+class Batch:
+    """Decode rows over a BlockPool with a host mirror of the device tables (pkv_batch_*)."""
+
+    def __init__(self, pool: "BlockPool", rows: int, width: int):
+        import numpy as np
+        self.pool, self.rows, self.width = pool, int(rows), int(width)
+        ptr = lib().pkv_batch_create(pool._h, self.rows, self.width)
+        if not ptr:
+            raise PagedKVError(PKV_EINVAL, last_error())
+        self._h = ctypes.c_void_p(ptr)
+        self._updates = np.empty((self.rows * self.width, 3), dtype=np.int32)
+        self._lens = np.empty(self.rows, dtype=np.int32)
+        self._copies = np.empty((self.rows, 2), dtype=np.int64)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.pkv_batch_destroy(h)
+            self._h = None
+
+    def set_row(self, row: int, seq: int):
+        _check(lib().pkv_batch_set_row(self._h, int(row), int(seq)))
+
+    def plan_step(self, tokens_per_row: int = 1):
+        """(updates int32 [n, 3], lens int32 [rows], copies int64 [k, 2]); views into reused buffers."""
+        nu, nc = ctypes.c_int64(0), ctypes.c_int64(0)
+        _check(lib().pkv_batch_plan_step(self._h, int(tokens_per_row), self._updates.ctypes.data,
+                                         self._updates.shape[0], ctypes.byref(nu), self._lens.ctypes.data,
+                                         self._copies.ctypes.data, self._copies.shape[0], ctypes.byref(nc)))
+        return self._updates[:nu.value], self._lens, self._copies[:nc.value]

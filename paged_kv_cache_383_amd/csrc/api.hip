@@ -188,6 +188,23 @@ extern "C" int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int64_t*
   return ok();
 }
 
+extern "C" int paged_kv_prepare_step(int32_t* block_tables, int32_t max_blocks_per_seq, int32_t* context_lens,
+                                     int32_t num_seqs, const int32_t* updates, int64_t num_updates,
+                                     const int32_t* new_lens, int64_t* slot_mapping, int32_t block_size,
+                                     int64_t num_blocks, void* stream) {
+  if (num_seqs < 0 || num_updates < 0) return fail(PKV_EINVAL, "num_seqs and num_updates must be >= 0");
+  if (max_blocks_per_seq <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PKV_EINVAL, "max_blocks_per_seq, block_size and num_blocks must be positive");
+  if (num_seqs == 0 && num_updates == 0) return ok();
+  if (!block_tables || !context_lens || (num_updates > 0 && !updates))
+    return fail(PKV_EINVAL, "null pointer among block_tables, context_lens, updates");
+  hipError_t e = pkv::launch_prepare_step(block_tables, max_blocks_per_seq, context_lens, num_seqs, updates,
+                                          num_updates, new_lens, slot_mapping, block_size, num_blocks,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "paged_kv_prepare_step launch");
+  return ok();
+}
+
 extern "C" int paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,

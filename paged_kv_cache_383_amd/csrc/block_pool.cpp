@@ -18,6 +18,7 @@
 //     blocks a free releases go back to the front in table order, so the next
 //     request receives exactly the space just released;
 //   * every operation is all-or-nothing: on PKV_ENOSPACE nothing changes.
+#include <algorithm>
 #include <deque>
 #include <new>
 #include <string>
@@ -213,6 +214,132 @@ extern "C" int pkv_pool_build_tables(const pkv_block_pool* p, const int64_t* seq
     int32_t* row = tables_out + int64_t(i) * width;
     for (int32_t j = 0; j < width; ++j) row[j] = j < int32_t(s.table.size()) ? s.table[size_t(j)] : -1;
     lens_out[i] = int32_t(s.tokens);
+  }
+  return pkv::set_error(PKV_OK, "");
+}
+
+// ---------------------------------------------------------------------------
+// Batch: the rows of a decode batch and a mirror of the device block tables.
+//
+// A decode step's metadata lives on the GPU ([card] "vLLM에서의 위치": the
+// worker keeps per-request block tables as device tensors).  Between two steps
+// only a few entries change: each sequence grows by one token, which opens a
+// new block every block_size steps, a copy-on-write replaces one entry, and a
+// row whose request ended is reassigned.  The batch keeps a host mirror of the
+// device tables, so each plan lists just the entries that differ; a kernel
+// (paged_kv_prepare_step) applies them and derives the slot mapping on the
+// device.
+struct pkv_batch {
+  pkv_block_pool* pool = nullptr;
+  int32_t rows = 0, width = 0;
+  std::vector<int64_t> seq;               // row -> sequence id, -1 = idle
+  std::vector<int32_t> mirror;            // [rows, width]: what the device tables hold
+  std::vector<int32_t> dirty_from;        // first column of the row that may differ (width = clean)
+};
+
+extern "C" pkv_batch* pkv_batch_create(pkv_block_pool* pool, int32_t rows, int32_t width) {
+  if (!pool || rows <= 0 || width <= 0) {
+    pool_fail(PKV_EINVAL, "null pool or non-positive rows / width");
+    return nullptr;
+  }
+  pkv_batch* b = new (std::nothrow) pkv_batch;
+  if (!b) {
+    pool_fail(PKV_EINVAL, "out of host memory");
+    return nullptr;
+  }
+  b->pool = pool;
+  b->rows = rows;
+  b->width = width;
+  b->seq.assign(size_t(rows), -1);
+  b->mirror.assign(size_t(rows) * size_t(width), -1);
+  b->dirty_from.assign(size_t(rows), width);
+  pkv::set_error(PKV_OK, "");
+  return b;
+}
+
+extern "C" void pkv_batch_destroy(pkv_batch* b) { delete b; }
+
+extern "C" int pkv_batch_set_row(pkv_batch* b, int32_t row, int64_t seq) {
+  if (!b || row < 0 || row >= b->rows) return pool_fail(PKV_EINVAL, "null batch or row out of range");
+  if (seq >= 0) {
+    auto it = b->pool->seqs.find(seq);
+    if (it == b->pool->seqs.end()) return pool_fail(PKV_EINVAL, "unknown sequence " + std::to_string(seq));
+    if (int64_t(it->second.table.size()) > b->width)
+      return pool_fail(PKV_EINVAL, "sequence " + std::to_string(seq) + " is wider than the batch tables");
+  }
+  b->seq[size_t(row)] = seq < 0 ? -1 : seq;
+  b->dirty_from[size_t(row)] = 0;
+  return pkv::set_error(PKV_OK, "");
+}
+
+extern "C" int pkv_batch_plan_step(pkv_batch* b, int32_t tokens_per_row, int32_t* updates_out, int64_t max_updates,
+                                   int64_t* n_updates, int32_t* lens_out, int64_t* copies_out, int64_t max_copies,
+                                   int64_t* n_copies) {
+  if (!b || tokens_per_row < 0 || !n_updates || !lens_out || !n_copies || !updates_out ||
+      (max_copies > 0 && !copies_out))
+    return pool_fail(PKV_EINVAL, "null batch or output pointer, or negative token count");
+  if (max_updates < int64_t(b->rows) * b->width)
+    return pool_fail(PKV_EINVAL, "updates_out must hold rows * width = " +
+                                     std::to_string(int64_t(b->rows) * b->width) + " entries");
+  pkv_block_pool* p = b->pool;
+  const int64_t bs = p->block_size;
+  // Check first, so that a failure changes nothing: every active row's
+  // sequence exists, stays within the table width, and the free list covers
+  // the step's new blocks and copies.
+  int64_t need = 0, copies = 0;
+  for (int32_t r = 0; r < b->rows; ++r) {
+    const int64_t s = b->seq[size_t(r)];
+    if (s < 0) continue;
+    auto it = p->seqs.find(s);
+    if (it == p->seqs.end())
+      return pool_fail(PKV_EINVAL, "row " + std::to_string(r) + " holds unknown sequence " + std::to_string(s));
+    const Sequence& q = it->second;
+    const int64_t nb = p->blocks_for(q.tokens + tokens_per_row);
+    if (nb > b->width)
+      return pool_fail(PKV_EINVAL, "sequence " + std::to_string(s) + " would outgrow the batch tables");
+    need += nb - int64_t(q.table.size());
+    if (tokens_per_row > 0 && q.tokens % bs != 0 && p->refcount[size_t(q.table.back())] > 1) {
+      ++need;
+      ++copies;
+    }
+  }
+  if (copies > max_copies) return pool_fail(PKV_EINVAL, "room for " + std::to_string(copies) + " copies is needed");
+  if (need > int64_t(p->free_list.size()))
+    return pool_fail(PKV_ENOSPACE, std::to_string(need) + " blocks needed, " +
+                                       std::to_string(p->free_list.size()) + " free");
+  // Count the updates before emitting any, for the same reason.
+  *n_updates = 0;
+  *n_copies = 0;
+  int64_t slot_tmp[1];
+  for (int32_t r = 0; r < b->rows; ++r) {
+    const int64_t s = b->seq[size_t(r)];
+    if (s < 0 || tokens_per_row == 0) continue;
+    Sequence& q = p->seqs.find(s)->second;
+    const int64_t first = q.tokens % bs != 0 ? int64_t(q.table.size()) - 1 : int64_t(q.table.size());
+    for (int32_t t = 0; t < tokens_per_row; ++t) {
+      int64_t nc = 0;
+      pkv_pool_append_slots(p, s, 1, slot_tmp, copies_out + 2 * *n_copies, max_copies - *n_copies, &nc);
+      *n_copies += nc;
+    }
+    int32_t& d = b->dirty_from[size_t(r)];
+    d = std::min<int32_t>(d, int32_t(std::max<int64_t>(first, 0)));
+  }
+  for (int32_t r = 0; r < b->rows; ++r) {
+    int32_t& d = b->dirty_from[size_t(r)];
+    const int64_t s = b->seq[size_t(r)];
+    const std::vector<int32_t>* t = s >= 0 ? &p->seqs.find(s)->second.table : nullptr;
+    lens_out[r] = s >= 0 ? int32_t(p->seqs.find(s)->second.tokens) : 0;
+    for (int32_t c = d; c < b->width; ++c) {
+      const int32_t want = (t && c < int32_t(t->size())) ? (*t)[size_t(c)] : -1;
+      int32_t& have = b->mirror[size_t(r) * b->width + c];
+      if (have == want) continue;
+      updates_out[3 * *n_updates] = r;
+      updates_out[3 * *n_updates + 1] = c;
+      updates_out[3 * *n_updates + 2] = want;
+      ++*n_updates;
+      have = want;
+    }
+    d = b->width;
   }
   return pkv::set_error(PKV_OK, "");
 }

@@ -67,4 +67,8 @@ hipError_t launch_kv_write(int dtype, int head_dim, const void* k, const void* v
 hipError_t launch_copy_blocks(const int64_t* block_mapping, int64_t num_pairs, void* k_cache, void* v_cache,
                               int64_t num_blocks, int64_t block_bytes, hipStream_t stream);
 
+hipError_t launch_prepare_step(int32_t* block_tables, int32_t width, int32_t* context_lens, int32_t rows,
+                               const int32_t* updates, int64_t n_updates, const int32_t* new_lens,
+                               int64_t* slot_mapping, int32_t block_size, int64_t num_blocks, hipStream_t stream);
+
 }  // namespace pkv

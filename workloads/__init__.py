@@ -297,3 +297,39 @@ def sampling_prompts(cfg: SamplingConfig, seed: int | None = None):
     needed = int(((lens + cfg.block_size - 1) // cfg.block_size).sum())
     nb = ceil_div(5 * needed, 4) + cfg.prompts * cfg.samples
     return lens.astype(np.int64), nb, rng.permutation(nb).astype(np.int32)
+
+
+# ---------------------------------------------------------------- continuous batching request stream
+
+@dataclass(frozen=True)
+class BatchingConfig:
+    """A continuous-batching decode loop ("vLLM KV cache and PagedAttention explained", Step 8) over
+    256 batch rows at the continuous-batching configuration's shape (32 heads, head_dim 128, 16-token
+    blocks, bf16): prompts lognormal around 512 tokens (clipped to [8, 4096]), each request generating
+    a uniform [16, 512] number of tokens; a finished request's row takes the next request at once."""
+    name: str = "continuous_batching_256rows_h32_d128_bf16_prompt_lognormal512_gen16-512"
+    rows: int = 256
+    num_heads: int = 32
+    head_dim: int = 128
+    block_size: int = 16
+    dtype: str = BF16
+    prompt_median: float = 512.0
+    prompt_sigma: float = 1.0
+    prompt_min: int = 8
+    prompt_max: int = 4096
+    gen_min: int = 16
+    gen_max: int = 512
+    seed: int = SEED_BASE + 200
+
+    @property
+    def width(self) -> int:
+        return ceil_div(self.prompt_max + self.gen_max, self.block_size)
+
+
+def batching_requests(cfg: BatchingConfig, n: int, seed: int | None = None):
+    """Prompt and generation lengths of ``n`` requests, in arrival order."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    prompts = np.clip(np.rint(np.exp(rng.normal(math.log(cfg.prompt_median), cfg.prompt_sigma, n))),
+                      cfg.prompt_min, cfg.prompt_max).astype(np.int64)
+    gens = rng.integers(cfg.gen_min, cfg.gen_max + 1, n).astype(np.int64)
+    return prompts, gens
