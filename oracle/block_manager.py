@@ -143,6 +143,41 @@ class BlockPool:
         return t, lens
 
 
+def usage(pool: BlockPool) -> dict:
+    """Slot accounting of a pool (the pages' waste comparison, [explain] "Why Waste Stays Below 4%"
+    and the Korean step-6 calculation).
+
+    used_blocks      blocks held by at least one table
+    allocated_slots  used_blocks * block_size
+    stored_tokens    slots that hold a token: each used block counts the
+                     filled slots of its fullest holder, once however many
+                     tables share it
+    logical_tokens   sum of the sequences' lengths (a shared token counts once
+                     per sequence that reads it)
+    """
+    bs = pool.block_size
+    fill = {}
+    for seq, table in pool.tables.items():
+        n = pool.tokens[seq]
+        for j, b in enumerate(table):
+            fill[b] = max(fill.get(b, 0), min(bs, n - j * bs))
+    return {"num_blocks": pool.num_blocks, "free_blocks": len(pool.free), "used_blocks": len(fill),
+            "sequences": len(pool.tables), "logical_tokens": sum(pool.tokens.values()),
+            "stored_tokens": sum(fill.values()), "allocated_slots": len(fill) * bs,
+            "shared_blocks": sum(1 for b in fill if pool.refcount[b] > 1)}
+
+
+def paged_waste(u: dict) -> float:
+    """Fraction of the allocated slots that hold no token (empty tail slots)."""
+    return 1.0 - u["stored_tokens"] / u["allocated_slots"] if u["allocated_slots"] else 0.0
+
+
+def static_waste(u: dict, max_model_len: int) -> float:
+    """Fraction wasted if every sequence had reserved max_model_len contiguous slots instead."""
+    reserved = u["sequences"] * int(max_model_len)
+    return 1.0 - u["logical_tokens"] / reserved if reserved else 0.0
+
+
 def copy_blocks(k_cache, v_cache, copies):
     """New cache arrays with block ``dst`` holding what block ``src`` held, for each (src, dst).
 

@@ -608,5 +608,42 @@ def pin_copy_blocks(bm, o):
     assert np.array_equal(v2[untouched].view(np.uint32), v[untouched].view(np.uint32))
 
 
+def pin_pool_waste_example(bm, o):
+    """The pages' A100 / LLaMA-2-13B comparison: static reservation vs 16-token blocks."""
+    g = golden("waste.json")
+    bs, mb = g["block_size"], g["mb_per_token"]
+    pool = bm.BlockPool(100, bs)
+    for i, L in enumerate(g["lens"]):
+        pool.allocate(i, L)
+    u = bm.usage(pool)
+    assert u["used_blocks"] == g["paged_blocks"] and u["stored_tokens"] == g["used_tokens"]
+    assert u["logical_tokens"] == g["used_tokens"] and u["sequences"] == len(g["lens"])
+    assert u["allocated_slots"] - u["stored_tokens"] == g["empty_slots"]
+    assert [len(pool.table(i)) * bs - L for i, L in enumerate(g["lens"])] == g["empty_slots_per_request"]
+    assert abs(bm.paged_waste(u) - g["paged_waste"]) < 1e-12
+    static = u["sequences"] * g["max_model_len"]
+    assert static == g["static_slots"]
+    assert abs(static * mb - g["static_mb_approx"]) / g["static_mb_approx"] < 0.01
+    assert abs(u["stored_tokens"] * mb - g["used_mb_approx"]) < 1.0
+    assert abs(u["allocated_slots"] * mb - g["paged_mb_approx"]) < 1.0
+    assert round(bm.static_waste(u, g["max_model_len"]), 2) == g["static_waste_approx"]
+    for L, empty in g["why_below_4_percent"]["cases"]:
+        p = bm.BlockPool(8, bs)
+        p.allocate(0, L)
+        uu = bm.usage(p)
+        assert uu["allocated_slots"] - uu["stored_tokens"] == empty
+    # sharing: a forked prompt's blocks are stored once but read by both sequences
+    p = bm.BlockPool(16, bs)
+    p.allocate(0, 40)
+    p.fork(0, 1)
+    uu = bm.usage(p)
+    assert uu["stored_tokens"] == 40 and uu["logical_tokens"] == 80 and uu["shared_blocks"] == 3
+    assert abs(bm.paged_waste(uu) - 8 / 48) < 1e-12            # the third block's 8 empty slots
+    p.append_slots(1, 1)                       # copy-on-write of the partly filled third block
+    uu = bm.usage(p)
+    assert uu["stored_tokens"] == 16 + 16 + 8 + 9 and uu["used_blocks"] == 4 and uu["shared_blocks"] == 2
+
+
 POOL_PINS = [pin_pool_block42_flow, pin_pool_prefix_full_block, pin_pool_copy_on_write,
-             pin_pool_parallel_sampling, pin_pool_invariants, pin_pool_contents, pin_copy_blocks]
+             pin_pool_parallel_sampling, pin_pool_invariants, pin_pool_contents, pin_copy_blocks,
+             pin_pool_waste_example]

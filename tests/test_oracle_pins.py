@@ -287,7 +287,27 @@ def _copy_backwards(k_cache, v_cache, copies):
         (np.array(k_cache, copy=True), np.array(v_cache, copy=True))
 
 
+def _usage_counts_holders(pool):
+    u = _orig("usage")(pool)
+    bs = pool.block_size
+    u["stored_tokens"] = sum(min(bs, pool.tokens[s] - j * bs) for s, t in pool.tables.items() for j in range(len(t)))
+    return u
+
+
+def _usage_counts_free_blocks(pool):
+    u = _orig("usage")(pool)
+    u["allocated_slots"] = pool.num_blocks * pool.block_size
+    return u
+
+
+def _waste_from_logical(u):
+    return 1.0 - u["logical_tokens"] / u["allocated_slots"] if u["allocated_slots"] else 0.0
+
+
 POOL_MUTANTS = {
+    "usage counts a shared block once per holder": ("usage", _usage_counts_holders),
+    "usage counts free blocks as allocated": ("usage", _usage_counts_free_blocks),
+    "paged waste from logical tokens": ("paged_waste", _waste_from_logical),
     "append never copies a shared block": ("BlockPool.append_slots", _append_no_cow),
     "copy-on-write keeps the source's count": ("BlockPool.append_slots", _append_cow_keeps_count),
     "copy pairs reversed": ("BlockPool.append_slots", _append_reversed_copies),
