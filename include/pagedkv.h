@@ -266,6 +266,22 @@ int64_t pkv_pool_num_tokens(const pkv_block_pool* pool, int64_t seq);
 int64_t pkv_pool_table(const pkv_block_pool* pool, int64_t seq, int32_t* out, int64_t cap);
 int64_t pkv_pool_free_list(const pkv_block_pool* pool, int32_t* out, int64_t cap);
 
+/* Slot accounting ([explain] "Why Waste Stays Below 4%" and the step-6 waste
+ * calculation).  Paged waste = 1 - stored_tokens / allocated_slots (the empty
+ * tail slots of each sequence's last block); static-reservation waste for a
+ * maximum length M = 1 - logical_tokens / (sequences * M). */
+typedef struct {
+  int64_t num_blocks;
+  int64_t free_blocks;
+  int64_t used_blocks;      /* blocks held by at least one table                          */
+  int64_t sequences;
+  int64_t logical_tokens;   /* sum of sequence lengths (a shared token once per reader)   */
+  int64_t stored_tokens;    /* filled slots of used blocks, a shared block counted once   */
+  int64_t allocated_slots;  /* used_blocks * block_size                                   */
+  int64_t shared_blocks;    /* used blocks held by more than one table                    */
+} pkv_pool_usage_t;
+int pkv_pool_usage(const pkv_block_pool* pool, pkv_pool_usage_t* out);
+
 /*
  * ---- Batch: decode rows over a pool, with a mirror of the device tables ----
  *

@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
             "pkv_pool_num_free": ([vp], i64), "pkv_pool_refcount": ([vp, i64], i32),
             "pkv_pool_num_tokens": ([vp, i64], i64), "pkv_pool_table": ([vp, i64, vp, i64], i64),
             "pkv_pool_free_list": ([vp, vp, i64], i64),
+            "pkv_pool_usage": ([vp, vp], ctypes.c_int),
             "pkv_batch_create": ([vp, i32, i32], vp), "pkv_batch_destroy": ([vp], None),
             "pkv_batch_set_row": ([vp, i32, i64], ctypes.c_int),
             "pkv_batch_plan_step": ([vp, i32, vp, i64, vp, vp, vp, i64, vp], ctypes.c_int),
@@ -270,6 +271,15 @@ class BlockPool:
 
     def refcount(self, block: int) -> int:
         return int(lib().pkv_pool_refcount(self._h, int(block)))
+
+    def usage(self) -> dict:
+        """Slot accounting: blocks used / free, stored vs logical tokens, allocated slots, shared blocks."""
+        import numpy as np
+        names = ("num_blocks", "free_blocks", "used_blocks", "sequences", "logical_tokens", "stored_tokens",
+                 "allocated_slots", "shared_blocks")
+        buf = np.zeros(len(names), dtype=np.int64)
+        _check(lib().pkv_pool_usage(self._h, buf.ctypes.data))
+        return dict(zip(names, (int(x) for x in buf)))
 
     def free_list(self):
         import numpy as np

@@ -195,6 +195,38 @@ extern "C" int64_t pkv_pool_free_list(const pkv_block_pool* p, int32_t* out, int
   return int64_t(p->free_list.size());
 }
 
+extern "C" int pkv_pool_usage(const pkv_block_pool* p, pkv_pool_usage_t* out) {
+  if (!p || !out) return pool_fail(PKV_EINVAL, "null pool or output");
+  // A used block stores the filled slots of its fullest holder, once, however
+  // many tables share it.
+  std::vector<int32_t> fill(size_t(p->num_blocks), -1);
+  const int64_t bs = p->block_size;
+  int64_t logical = 0;
+  for (const auto& kv : p->seqs) {
+    const Sequence& s = kv.second;
+    logical += s.tokens;
+    for (size_t j = 0; j < s.table.size(); ++j) {
+      const int64_t f = std::min<int64_t>(bs, s.tokens - int64_t(j) * bs);
+      int32_t& cur = fill[size_t(s.table[j])];
+      cur = std::max<int32_t>(cur, int32_t(f));
+    }
+  }
+  pkv_pool_usage_t u{};
+  u.num_blocks = p->num_blocks;
+  u.free_blocks = int64_t(p->free_list.size());
+  u.sequences = int64_t(p->seqs.size());
+  u.logical_tokens = logical;
+  for (int64_t b = 0; b < p->num_blocks; ++b) {
+    if (fill[size_t(b)] < 0) continue;
+    ++u.used_blocks;
+    u.stored_tokens += fill[size_t(b)];
+    if (p->refcount[size_t(b)] > 1) ++u.shared_blocks;
+  }
+  u.allocated_slots = u.used_blocks * bs;
+  *out = u;
+  return pkv::set_error(PKV_OK, "");
+}
+
 extern "C" int pkv_pool_build_tables(const pkv_block_pool* p, const int64_t* seqs, int32_t n, int32_t width,
                                      int32_t* tables_out, int32_t* lens_out) {
   if (!p || n < 0 || width <= 0 || (n > 0 && (!seqs || !tables_out || !lens_out)))
