@@ -158,6 +158,38 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, block_
     return out
 
 
+def prefill(q, k_cache, v_cache, block_tables, query_start, context_lens, scale: float, block_size: int,
+            dtype: str) -> np.ndarray:
+    """Causal attention of a batch of new tokens over their sequences' paged caches.
+
+    Sequence i brings the queries q[query_start[i] : query_start[i+1]] (P_i of
+    them) and holds L_i = context_lens[i] cached tokens, the last P_i of which
+    are these new tokens' own K/V (written before the call), so query j sits
+    at position p = L_i - P_i + j.  It attends to cached tokens 0 .. p and
+    never to a later one: the prefill phase processes all prompt tokens in
+    parallel ([explain] Step 6) with causal attention, each token seeing only
+    the tokens before it and itself ([explain] Summary: causal attention).  A
+    non-empty prefix L_i - P_i > 0 is a cached (e.g. shared) prompt prefix
+    ([explain] Step 9) or an earlier chunk.  Returns float64 [T, H, D].
+    """
+    q64 = to_float64(q, dtype)
+    T, H, D = q64.shape
+    out = np.zeros((T, H, D), dtype=np.float64)
+    qs = np.asarray(query_start).tolist()
+    for i in range(len(qs) - 1):
+        a, b = qs[i], qs[i + 1]
+        L = int(context_lens[i])
+        if b == a:
+            continue
+        K = gather_sequence(k_cache, block_tables[i], L, block_size, dtype)        # [H, L, D]
+        V = gather_sequence(v_cache, block_tables[i], L, block_size, dtype)
+        first = L - (b - a)                                                         # position of query 0
+        for j in range(b - a):
+            p = first + j
+            out[a + j] = attend(q64[a + j], K[:, :p + 1], V[:, :p + 1], scale)
+    return out
+
+
 def partition_state(q, K, V, scale: float):
     """(m, l, acc) of one context partition, per head.
 

@@ -409,10 +409,82 @@ def pin_newest_token_slots(o):
         assert np.array_equal(c.k_pool[b, :, off, :], c.Klog[i][L - 1])
 
 
+def _prefill_case(rng, lens, news, H=2, D=8, bs=16, dtype="f32"):
+    """A Case whose sequence i holds lens[i] tokens, the last news[i] of them new (with queries)."""
+    c = Case(rng, lens, H=H, D=D, bs=bs, dtype=dtype)
+    qs = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    if dtype == "f32":
+        q = rng.standard_normal((int(qs[-1]), H, D)).astype(np.float32)
+    else:
+        q = (rng.standard_normal((int(qs[-1]), H, D)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return c, q, qs
+
+
+def pin_prefill_brute_force(o):
+    """Every query row against textbook softmax over the tokens up to and including its own position."""
+    rng = np.random.default_rng(25)
+    for dtype in ("f32", "bf16"):
+        c, q, qs = _prefill_case(rng, [6, 20, 37], [6, 4, 37], dtype=dtype)
+        got = o.prefill(q, c.k_pool, c.v_pool, c.tables, qs, c.context_lens, c.scale, c.bs, dtype)
+        f = c.to_py
+        for i, L in enumerate(c.lens):
+            n = int(qs[i + 1] - qs[i])
+            K = [[[f(x) for x in r] for r in tok] for tok in c.Klog[i]]
+            V = [[[f(x) for x in r] for r in tok] for tok in c.Vlog[i]]
+            for j in range(n):
+                p = L - n + j
+                qq = [[f(x) for x in row] for row in q[qs[i] + j]]
+                want = np.array(brute_force(qq, K[:p + 1], V[:p + 1], c.scale))
+                assert np.max(np.abs(got[qs[i] + j] - want)) <= 1e-12, (dtype, i, j)
+
+
+def pin_prefill_closed_forms(o):
+    """The pages' 6-token prompt ([explain] Step 6): the first token sees only itself, so its output is
+    its own V row exactly; with q = 0 every row is the running mean of V."""
+    rng = np.random.default_rng(26)
+    c, q, qs = _prefill_case(rng, [6], [6], H=3, D=16)
+    out = o.prefill(q, c.k_pool, c.v_pool, c.tables, qs, c.context_lens, 0.7, c.bs, "f32")
+    assert np.array_equal(out[0], c.Vlog[0][0].astype(np.float64))
+    q[:] = 0
+    out = o.prefill(q, c.k_pool, c.v_pool, c.tables, qs, c.context_lens, 0.7, c.bs, "f32")
+    for j in range(6):
+        assert np.max(np.abs(out[j] - c.Vlog[0][:j + 1].astype(np.float64).mean(axis=0))) <= 1e-12
+
+
+def pin_prefill_causality(o):
+    """Changing a token's K/V changes the rows at or after its position and none before."""
+    rng = np.random.default_rng(27)
+    c, q, qs = _prefill_case(rng, [40], [40])
+    base = o.prefill(q, c.k_pool, c.v_pool, c.tables, qs, c.context_lens, c.scale, c.bs, "f32")
+    t = 23
+    b, off = c.tables[0][t // c.bs], t % c.bs
+    c.k_pool[b, :, off, :] += 1.0
+    c.v_pool[b, :, off, :] -= 2.0
+    moved = o.prefill(q, c.k_pool, c.v_pool, c.tables, qs, c.context_lens, c.scale, c.bs, "f32")
+    assert np.array_equal(moved[:t], base[:t])
+    assert np.all(np.max(np.abs(moved[t:] - base[t:]), axis=(1, 2)) > 0)
+
+
+def pin_prefill_prefix_chunks(o):
+    """A chunk of new tokens after a cached prefix ([explain] Step 9) gives the same rows as the
+    corresponding rows of one prefill over the whole prompt."""
+    rng = np.random.default_rng(28)
+    c, q, qs = _prefill_case(rng, [50, 33], [50, 33])
+    full = o.prefill(q, c.k_pool, c.v_pool, c.tables, qs, c.context_lens, c.scale, c.bs, "f32")
+    sel = np.concatenate([np.arange(50 - 14, 50), [50 + 32]])
+    part = o.prefill(q[sel], c.k_pool, c.v_pool, c.tables, np.array([0, 14, 15]), c.context_lens, c.scale,
+                     c.bs, "f32")
+    assert np.max(np.abs(part - full[sel])) <= 1e-12
+    # the last row of a prefill is the decode of that sequence
+    dec = o.decode(q[[49, 82]], c.k_pool, c.v_pool, c.tables, c.context_lens, c.scale, c.bs, "f32")
+    assert np.max(np.abs(dec - full[[49, 82]])) <= 1e-12
+
+
 PINS = [pin_block_counts, pin_storage_upcast, pin_round_to_storage, pin_slot_example,
         pin_write_then_read, pin_write_bitwise, pin_brute_force, pin_pages_tables,
         pin_permutation_invariance, pin_poison_invariance, pin_closed_forms,
-        pin_split_equals_single, pin_prefix_sharing, pin_newest_token_slots]
+        pin_split_equals_single, pin_prefix_sharing, pin_newest_token_slots, pin_prefill_brute_force,
+        pin_prefill_closed_forms, pin_prefill_causality, pin_prefill_prefix_chunks]
 
 
 # ---------------------------------------------------------------- block pool pins

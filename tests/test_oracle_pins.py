@@ -140,7 +140,39 @@ def _slots_position_l(block_tables, context_lens, block_size):
     return out
 
 
+def _prefill_core(q, k_cache, v_cache, block_tables, query_start, context_lens, scale, block_size, dtype, keys):
+    q64 = O.to_float64(q, dtype)
+    out = np.zeros(q64.shape, dtype=np.float64)
+    qs = np.asarray(query_start).tolist()
+    for i in range(len(qs) - 1):
+        a, b = qs[i], qs[i + 1]
+        L = int(context_lens[i])
+        if b == a:
+            continue
+        K = O.gather_sequence(k_cache, block_tables[i], L, block_size, dtype)
+        V = O.gather_sequence(v_cache, block_tables[i], L, block_size, dtype)
+        for j in range(b - a):
+            n = keys(L, b - a, j)
+            out[a + j] = O.attend(q64[a + j], K[:, :n], V[:, :n], scale)
+    return out
+
+
+def _prefill_not_causal(*a):
+    return _prefill_core(*a, keys=lambda L, n, j: L)
+
+
+def _prefill_excludes_self(*a):
+    return _prefill_core(*a, keys=lambda L, n, j: max(L - n + j, 1))
+
+
+def _prefill_ignores_prefix(*a):
+    return _prefill_core(*a, keys=lambda L, n, j: j + 1)
+
+
 MUTANTS = {
+    "prefill attends to later tokens": ("prefill", _prefill_not_causal),
+    "prefill query does not see itself": ("prefill", _prefill_excludes_self),
+    "prefill ignores the cached prefix": ("prefill", _prefill_ignores_prefix),
     "newest slot taken at position 1": ("newest_token_slots", _slots_oldest_token),
     "newest slot taken at position L": ("newest_token_slots", _slots_position_l),
     "blocks_needed floors": ("blocks_needed", _floor_blocks),
