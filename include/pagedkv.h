@@ -157,6 +157,41 @@ int paged_attention_decode(const void* q, const void* k_cache, const void* v_cac
                            int32_t partition_size, void* stream);
 
 /*
+ * paged_attention_prefill -- causal attention of a batch of new tokens over
+ * their sequences' paged caches (the prefill phase, [explain] Step 6: all
+ * prompt tokens are processed in parallel, each attending to the tokens before
+ * it and itself; Summary: causal attention).
+ *
+ * Sequence i brings the queries q[query_start[i] .. query_start[i+1]) (P_i of
+ * them) and holds L_i = context_lens[i] >= P_i cached tokens whose last P_i are
+ * these queries' own K/V, already written (paged_kv_write).  Query j sits at
+ * position p = L_i - P_i + j and
+ *   out[query_start[i] + j, h, :] = softmax_t( scale * q[.., h, :] . K_i[t, h, :] ) V_i[t, h, :],  t in [0, p]
+ * with K_i, V_i read through block_tables as in paged_attention_decode.  Tokens
+ * before the new ones (L_i - P_i > 0) are a cached prefix: an earlier chunk of
+ * the prompt, or blocks shared with other requests ([explain] Step 9).
+ *
+ *   q             [T, num_heads, head_dim], dtype, T = query_start[num_seqs]
+ *   k_cache,
+ *   v_cache       [num_blocks, num_heads, block_size, head_dim], dtype
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32
+ *   query_start   [num_seqs + 1] int32, non-decreasing, query_start[0] = 0
+ *   context_lens  [num_seqs] int32
+ *   max_query_len at least every P_i (sizes the grid)
+ *   out           [T, num_heads, head_dim], dtype, written
+ * Runs on the matrix cores (MFMA) with fp32 accumulation; the output is
+ * rounded to nearest even.  Caller contract, checked under PKV_DEBUG=1:
+ * P_i <= max_query_len, P_i <= L_i <= max_blocks_per_seq * block_size, block ids
+ * in range; a sequence that breaks it gets NaN rows, and no memory outside the
+ * arrays is touched.  Returns PKV_OK, or an error status with nothing launched.
+ */
+int paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* query_start, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t max_query_len, int32_t num_heads, int32_t head_dim,
+                            int32_t block_size, int64_t num_blocks, float scale, int32_t dtype, void* out,
+                            void* stream);
+
+/*
  * paged_kv_copy_blocks -- copy whole physical blocks, K and V: for every pair
  * i, block block_mapping[2i+1] of each pool receives the contents of block
  * block_mapping[2i].  This is the copy in copy-on-write ([explain] Step 9: a

@@ -13,6 +13,8 @@ If the library is not built, every call raises.
                                     max_blocks_per_seq, block_size, partition_size)
     paged_attention_partition_size(num_seqs, num_heads, max_blocks_per_seq, block_size,
                                    partition_size)
+    paged_attention_prefill(q, k_cache, v_cache, block_tables, query_start, context_lens, scale,
+                            max_query_len, out=None)
     paged_kv_copy_blocks(k_cache, v_cache, block_mapping)
     BlockPool(num_blocks, block_size, free_order=None): allocate, fork, append_slots,
         free_sequence, build_tables, table, num_tokens, num_free, refcount, free_list
@@ -76,6 +78,8 @@ def lib() -> ctypes.CDLL:
             "pkv_pool_num_tokens": ([vp, i64], i64), "pkv_pool_table": ([vp, i64, vp, i64], i64),
             "pkv_pool_free_list": ([vp, vp, i64], i64),
             "pkv_pool_usage": ([vp, vp], ctypes.c_int),
+            "paged_attention_prefill": ([vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i64,
+                                         ctypes.c_float, i32, vp, vp], ctypes.c_int),
             "pkv_batch_create": ([vp, i32, i32], vp), "pkv_batch_destroy": ([vp], None),
             "pkv_batch_set_row": ([vp, i32, i64], ctypes.c_int),
             "pkv_batch_plan_step": ([vp, i32, vp, i64, vp, vp, vp, i64, vp], ctypes.c_int),
@@ -189,6 +193,37 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
                                             bs, NB, float(scale), _dtype_code(q), out.data_ptr(),
                                             workspace.data_ptr(), ws_bytes, partition_size,
                                             _stream(q.device)))
+    return out
+
+
+def paged_attention_prefill(q, k_cache, v_cache, block_tables, query_start, context_lens, scale,
+                            max_query_len: int, out=None):
+    """Causal attention of packed new tokens q [T, H, D] over their sequences' paged caches; sequence i owns
+    q[query_start[i]:query_start[i+1]] and context_lens[i] cached tokens ending with those tokens' K/V."""
+    import torch
+    _device_tensor("q", q, k_cache.dtype, 3)
+    _device_tensor("k_cache", k_cache, None, 4)
+    _device_tensor("v_cache", v_cache, k_cache.dtype, 4)
+    _device_tensor("block_tables", block_tables, torch.int32, 2)
+    _device_tensor("query_start", query_start, torch.int32, 1)
+    _device_tensor("context_lens", context_lens, torch.int32, 1)
+    NB, H, bs, D = k_cache.shape
+    B = context_lens.shape[0]
+    if v_cache.shape != k_cache.shape or q.shape[1:] != (H, D):
+        raise ValueError("q [T, H, D] and caches [NB, H, bs, D] do not match")
+    if block_tables.shape[0] != B or query_start.shape[0] != B + 1:
+        raise ValueError("block_tables needs one row and query_start B + 1 entries")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _device_tensor("out", out, q.dtype, 3)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    with torch.cuda.device(q.device):
+        _check(lib().paged_attention_prefill(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                             block_tables.data_ptr(), block_tables.shape[1], query_start.data_ptr(),
+                                             context_lens.data_ptr(), B, int(max_query_len), H, D, bs, NB,
+                                             float(scale), _dtype_code(q), out.data_ptr(), _stream(q.device)))
     return out
 
 

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libpagedkv.so")
-SOURCES = ["api.hip", "kv_write.hip", "decode.hip", "copy_blocks.hip", "step.hip", "block_pool.cpp"]
+SOURCES = ["api.hip", "kv_write.hip", "decode.hip", "copy_blocks.hip", "step.hip", "prefill.hip", "block_pool.cpp"]
 ARCH = "gfx950"
 
 

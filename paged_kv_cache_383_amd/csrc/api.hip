@@ -205,6 +205,70 @@ extern "C" int paged_kv_prepare_step(int32_t* block_tables, int32_t max_blocks_p
   return ok();
 }
 
+extern "C" int paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* query_start, const int32_t* context_lens, int32_t num_seqs,
+                                       int32_t max_query_len, int32_t num_heads, int32_t head_dim,
+                                       int32_t block_size, int64_t num_blocks, float scale, int32_t dtype,
+                                       void* out, void* stream) {
+  if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (int rc = check_shape(dtype, num_heads, head_dim, block_size, num_blocks)) return rc;
+  if (max_blocks_per_seq <= 0)
+    return fail(PKV_EINVAL, "max_blocks_per_seq must be positive (got %d)", max_blocks_per_seq);
+  if (int64_t(max_blocks_per_seq) * block_size > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "table capacity of %lld tokens exceeds int32", (long long)max_blocks_per_seq * block_size);
+  if (max_query_len < 0) return fail(PKV_EINVAL, "max_query_len must be >= 0 (got %d)", max_query_len);
+  if (!isfinite(scale)) return fail(PKV_EINVAL, "scale must be finite");
+  if (num_seqs == 0 || max_query_len == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !query_start || !context_lens || !out)
+    return fail(PKV_EINVAL, "null pointer among q, k_cache, v_cache, block_tables, query_start, context_lens, out");
+  const int64_t tiles = (int64_t(max_query_len) + pkv::prefill_tile_queries() - 1) / pkv::prefill_tile_queries();
+  if (num_heads > 65535 || num_seqs > 65535 || tiles > 65535)
+    return fail(PKV_EUNSUPPORTED, "grid (%d heads, %lld query tiles, %d sequences) exceeds 65535", num_heads,
+                (long long)tiles, num_seqs);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    std::vector<int32_t> qs(size_t(num_seqs) + 1), lens(num_seqs), tab(size_t(num_seqs) * max_blocks_per_seq);
+    hipError_t e = hipMemcpyAsync(qs.data(), query_start, qs.size() * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(lens.data(), context_lens, lens.size() * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(tab.data(), block_tables, tab.size() * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "PKV_DEBUG copy of metadata");
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      const int64_t P = int64_t(qs[i + 1]) - qs[i], L = lens[i];
+      if (P < 0 || P > max_query_len)
+        return fail(PKV_EINVAL, "sequence %d has %lld queries, outside [0, max_query_len = %d]", i, (long long)P,
+                    max_query_len);
+      if (L < P || L > int64_t(max_blocks_per_seq) * block_size)
+        return fail(PKV_EINVAL, "context_lens[%d] = %lld outside [%lld queries, %lld]", i, (long long)L,
+                    (long long)P, (long long)max_blocks_per_seq * block_size);
+      for (int64_t j = 0; j < (L + block_size - 1) / block_size; ++j) {
+        const int32_t b = tab[size_t(i) * max_blocks_per_seq + j];
+        if (b < 0 || b >= num_blocks)
+          return fail(PKV_EINVAL, "block_tables[%d, %lld] = %d outside [0, %lld)", i, (long long)j, b,
+                      (long long)num_blocks);
+      }
+    }
+  }
+  pkv::PrefillArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.query_start = query_start;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.max_query_len = max_query_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = pkv::launch_prefill(dtype, head_dim, block_size, a, st);
+  if (e != hipSuccess) return hip_fail(e, "paged_attention_prefill launch");
+  return ok();
+}
+
 extern "C" int paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,

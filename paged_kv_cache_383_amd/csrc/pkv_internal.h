@@ -71,4 +71,24 @@ hipError_t launch_prepare_step(int32_t* block_tables, int32_t width, int32_t* co
                                const int32_t* updates, int64_t n_updates, const int32_t* new_lens,
                                int64_t* slot_mapping, int32_t block_size, int64_t num_blocks, hipStream_t stream);
 
+struct PrefillArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* query_start;
+  const int32_t* context_lens;
+  void* out;
+  int64_t num_blocks;
+  int32_t max_blocks;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t max_query_len;
+  float scale_log2;
+};
+
+// Queries per prefill work-group (the grid's y extent is ceil(max_query_len / this)).
+int prefill_tile_queries();
+hipError_t launch_prefill(int dtype, int head_dim, int block_size, const PrefillArgs& a, hipStream_t stream);
+
 }  // namespace pkv

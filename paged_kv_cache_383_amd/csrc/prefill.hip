@@ -1,0 +1,344 @@
+// Paged prefill for gfx950: causal attention of a batch of new tokens over
+// their sequences' block-paged K/V caches, on the matrix cores.
+//
+// What is computed ("vLLM KV cache and PagedAttention explained", hrletsgo.me,
+// Step 6 and Appendix: The Attention Score Formula): a sequence's prompt
+// tokens are processed in parallel, each attending, by softmax(q K^T * scale) V,
+// to the cached tokens up to and including its own position (causal
+// attention).  The new tokens' K/V are already in the cache (paged_kv_write);
+// tokens before them (a cached or shared prefix, Step 9) are read the same
+// way, through the block table, in place ("PagedAttention" card, "Kernel은
+// 무엇이 달라지는가").
+//
+// Unlike decode, this is a dense contraction: a tile of queries meets every
+// key of a chunk, so the products go to MFMA.  Work decomposition: one
+// work-group of 4 wave64s per (head, 128-query tile, sequence); each wave owns
+// 32 queries as two 16-query sub-tiles.  Keys are walked in chunks of 32
+// (one 32-token block or two 16-token blocks), staged once per work-group in
+// LDS and shared by its 4 waves:
+//   K chunk as [key][d] (the cache's own row order),
+//   V chunk transposed as [d][key], so each lane's MFMA operand is a run of
+//   consecutive keys.
+// Per chunk and sub-tile a wave computes S^T = K Q^T with
+// v_mfma_f32_16x16x32_{bf16,f16} (fp32: 16x16x4), keeps each query's running
+// max across its four lane groups, and accumulates O^T += V^T P^T with P^T
+// taken straight from the S^T registers: a lane of S^T holds keys
+// {4g..4g+3} and {16+4g..16+4g+3} of one query (g = lane / 16), and the V^T
+// operand lists the same keys in the same k-slot order, so no transpose of P
+// is needed.  Keys past the query's position or past the context are masked;
+// their V rows are staged as zeros so that 0 * garbage never enters a sum.
+#include <hip/hip_fp16.h>
+
+#include "pagedkv.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSub = 2;                        // 16-query sub-tiles per wave
+constexpr int kTileQ = kWaves * kSub * 16;     // queries per work-group
+constexpr int kChunk = 32;                     // keys per chunk
+constexpr float kEmptyMax = -3.0e38f;
+
+template <int DT>
+struct Mfma;
+
+// 16-bit types: 16x16x32, 8 elements per lane per operand.
+template <>
+struct Mfma<PKV_BF16> {
+  static constexpr int kStep = 32, kEpl = 8, kBytes = 2;
+  using frag = bf16x8;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ __bf16 from_f32(float x) { return static_cast<__bf16>(x); }
+};
+template <>
+struct Mfma<PKV_F16> {
+  static constexpr int kStep = 32, kEpl = 8, kBytes = 2;
+  using frag = f16x8;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ _Float16 from_f32(float x) { return _Float16(x); }
+};
+// fp32: 16x16x4, one element per lane per operand.
+template <>
+struct Mfma<PKV_F32> {
+  static constexpr int kStep = 4, kEpl = 1, kBytes = 4;
+  using frag = float;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float from_f32(float x) { return x; }
+};
+
+template <int DT>
+using elem_t = typename std::conditional<DT == PKV_BF16, __bf16,
+                                         typename std::conditional<DT == PKV_F16, _Float16, float>::type>::type;
+
+__device__ __forceinline__ unsigned short f32_to_bf16_rne(float x) {
+  unsigned int u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<unsigned short>(u >> 16);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_out(void* base, int64_t i, float x) {
+  if constexpr (DT == PKV_F32) {
+    static_cast<float*>(base)[i] = x;
+  } else if constexpr (DT == PKV_F16) {
+    static_cast<unsigned short*>(base)[i] = __half_as_ushort(__float2half(x));
+  } else {
+    static_cast<unsigned short*>(base)[i] = f32_to_bf16_rne(x);
+  }
+}
+
+template <int DT, int D>
+struct Smem {
+  using E = elem_t<DT>;
+  static constexpr int kPadK = 16 / Mfma<DT>::kBytes;     // one 16-byte pad per K row
+  static constexpr int kPitchK = D + kPadK;
+  static constexpr int kPitchV = kChunk + 16 / Mfma<DT>::kBytes;
+  alignas(16) E k[kChunk * kPitchK];
+  alignas(16) E vt[D * kPitchV];
+};
+
+template <int DT, int D, int BS>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(
+    const void* __restrict__ q, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ query_start,
+    const int32_t* __restrict__ context_lens, void* __restrict__ out, int64_t num_blocks, int32_t max_blocks,
+    int32_t tiles, float scale_log2) {
+  using M = Mfma<DT>;
+  using E = elem_t<DT>;
+  using S = Smem<DT, D>;
+  constexpr int kEs = M::kBytes;
+  constexpr int kVpr = D * kEs / 16;                 // 16-byte vectors per K/V row
+  constexpr int kVecs = kChunk * kVpr;               // per chunk per tensor
+  constexpr int kEpv = 16 / kEs;                     // elements per 16-byte vector
+  constexpr int kDSteps = D / M::kStep;              // MFMA k-steps over head_dim
+  constexpr int kDTiles = D / 16;                    // 16-dim output tiles
+  __shared__ S sm;
+  __shared__ int sm_bad;
+
+  const int h = blockIdx.x;
+  const int tile = tiles - 1 - int(blockIdx.y);      // longest-running tiles first
+  const int s = blockIdx.z;
+  const int H = gridDim.x;
+  const int qa = query_start[s], qb = query_start[s + 1];
+  const int P = qb - qa;
+  const int L = context_lens[s];
+  const int q0 = tile * kTileQ;
+  if (P <= 0 || q0 >= P) return;
+  // Broken contract (more queries than context, a context past the table, or
+  // more queries than max_query_len covers): the sequence's rows become NaN
+  // and no cache memory is touched.
+  const bool ok = P <= L && L <= max_blocks * BS && P <= tiles * kTileQ;
+  const int first = L - P;                           // position of the sequence's first query
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;                         // query within a sub-tile (column of S^T)
+  const int grp = lane >> 4;                         // lane group: keys 4g.., dims 4g..
+
+  if (!ok) {
+    const int hi = tile == tiles - 1 ? P : min(q0 + kTileQ, P);     // the last tile also covers the rest
+    for (int64_t i = threadIdx.x; i < int64_t(hi - q0) * D; i += kThreads)
+      store_out<DT>(out, (int64_t(qa + q0 + int(i / D)) * H + h) * D + i % D, __builtin_nanf(""));
+    return;
+  }
+  if (threadIdx.x == 0) sm_bad = 0;
+
+  // Query fragments (B operand of S^T = K Q^T): lane holds Q[col][step * kStep + grp * kEpl + e].
+  typename M::frag qf[kSub][kDSteps];
+  int qpos[kSub];
+#pragma unroll
+  for (int u = 0; u < kSub; ++u) {
+    const int qi = q0 + (wave * kSub + u) * 16 + col;
+    qpos[u] = qi < P ? first + qi : -1;              // -1: no query (every key masked)
+    const E* qrow = static_cast<const E*>(q) + (int64_t(qa + (qi < P ? qi : 0)) * H + h) * D;
+#pragma unroll
+    for (int st = 0; st < kDSteps; ++st) {
+      if constexpr (M::kEpl == 1) {
+        qf[u][st] = qi < P ? qrow[st * M::kStep + grp] : 0.f;
+      } else {
+        const u32x4 raw = qi < P ? *reinterpret_cast<const u32x4*>(qrow + st * M::kStep + grp * M::kEpl)
+                                 : u32x4{0, 0, 0, 0};
+        qf[u][st] = __builtin_bit_cast(typename M::frag, raw);
+      }
+    }
+  }
+
+  f32x4 acc[kSub][kDTiles];
+  float m[kSub], l[kSub];
+#pragma unroll
+  for (int u = 0; u < kSub; ++u) {
+    m[u] = kEmptyMax;
+    l[u] = 0.f;
+#pragma unroll
+    for (int t = 0; t < kDTiles; ++t) acc[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Keys this work-group needs: up to its last query's position.
+  const int last_q = min(q0 + kTileQ, P) - 1;
+  const int nkeys = first + last_q + 1;
+  const int nchunks = (nkeys + kChunk - 1) / kChunk;
+  const int32_t* trow = block_tables + int64_t(s) * max_blocks;
+  bool bad = false;
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int k0 = c * kChunk;
+    // Stage the chunk: K as [key][d], V transposed as [d][key]; keys past the
+    // context are zeros.
+    for (int v = threadIdx.x; v < kVecs; v += kThreads) {
+      const int key = v / kVpr, cv = v % kVpr;
+      const int kg = k0 + key;
+      u32x4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+      if (kg < L) {
+        const int32_t b = trow[kg / BS];
+        if (static_cast<uint64_t>(static_cast<int64_t>(b)) < static_cast<uint64_t>(num_blocks)) {
+          const int64_t off = ((int64_t(b) * H + h) * BS + kg % BS) * int64_t(D * kEs) + cv * 16;
+          kk = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_cache + off));
+          vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_cache + off));
+        } else {
+          bad = true;
+        }
+      }
+      *reinterpret_cast<u32x4*>(&sm.k[key * S::kPitchK + cv * kEpv]) = kk;
+      const E* ve = reinterpret_cast<const E*>(&vv);
+#pragma unroll
+      for (int e = 0; e < kEpv; ++e) sm.vt[(cv * kEpv + e) * S::kPitchV + key] = ve[e];
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
+      // S^T for keys [k0, k0 + 32): two 16-key tiles.
+      f32x4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < kDSteps; ++st) {
+        typename M::frag a0, a1;
+        if constexpr (M::kEpl == 1) {
+          a0 = sm.k[col * S::kPitchK + st * M::kStep + grp];
+          a1 = sm.k[(16 + col) * S::kPitchK + st * M::kStep + grp];
+        } else {
+          a0 = __builtin_bit_cast(typename M::frag,
+                                  *reinterpret_cast<const u32x4*>(&sm.k[col * S::kPitchK + st * M::kStep + grp * M::kEpl]));
+          a1 = __builtin_bit_cast(typename M::frag,
+                                  *reinterpret_cast<const u32x4*>(&sm.k[(16 + col) * S::kPitchK + st * M::kStep + grp * M::kEpl]));
+        }
+        st0 = M::mma(a0, qf[u][st], st0);
+        st1 = M::mma(a1, qf[u][st], st1);
+      }
+      // Scale, mask (key position > query position, or past the context), running max.
+      float sc[8];
+      float bm = kEmptyMax;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ka = k0 + 4 * grp + e, kb = k0 + 16 + 4 * grp + e;
+        sc[e] = ka <= qpos[u] ? st0[e] * scale_log2 : -__builtin_inff();
+        sc[4 + e] = kb <= qpos[u] ? st1[e] * scale_log2 : -__builtin_inff();
+        bm = fmaxf(bm, fmaxf(sc[e], sc[4 + e]));
+      }
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float m_new = fmaxf(m[u], bm);
+      const float alpha = __builtin_amdgcn_exp2f(m[u] - m_new);
+      m[u] = m_new;
+      float p[8];
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(sc[e] - m_new);
+        ps += p[e];
+      }
+      l[u] = l[u] * alpha + ps;                      // this lane's share; groups summed at the end
+#pragma unroll
+      for (int t = 0; t < kDTiles; ++t) acc[u][t] *= alpha;
+      // O^T += V^T P^T.
+      if constexpr (M::kEpl == 1) {
+#pragma unroll
+        for (int t = 0; t < kDTiles; ++t) {
+          const E* vrow = &sm.vt[(16 * t + col) * S::kPitchV];
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[u][t] = M::mma(vrow[16 * half + 4 * grp + e], p[4 * half + e], acc[u][t]);
+        }
+      } else {
+        typename M::frag pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[e] = M::from_f32(p[e]);
+#pragma unroll
+        for (int t = 0; t < kDTiles; ++t) {
+          const E* vrow = &sm.vt[(16 * t + col) * S::kPitchV];
+          typename M::frag vf;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * grp);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * grp);
+          vf = __builtin_bit_cast(typename M::frag, u32x4{lo.x, lo.y, hi.x, hi.y});
+          acc[u][t] = M::mma(vf, pf, acc[u][t]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (bad) sm_bad = 1;
+  __syncthreads();
+  const bool any_bad = sm_bad != 0;
+#pragma unroll
+  for (int u = 0; u < kSub; ++u) {
+    const int qi = q0 + (wave * kSub + u) * 16 + col;
+    float lt = l[u];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (qi >= P) continue;
+    const float inv = any_bad ? __builtin_nanf("") : 1.f / lt;
+    const int64_t base = (int64_t(qa + qi) * H + h) * D;
+#pragma unroll
+    for (int t = 0; t < kDTiles; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_out<DT>(out, base + 16 * t + 4 * grp + e, acc[u][t][e] * inv);
+  }
+}
+
+template <int DT, int D, int BS>
+hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
+  const int tiles = (a.max_query_len + kTileQ - 1) / kTileQ;
+  const dim3 grid(unsigned(a.num_heads), unsigned(tiles), unsigned(a.num_seqs));
+  hipLaunchKernelGGL((prefill_kernel<DT, D, BS>), grid, dim3(kThreads), 0, stream, a.q,
+                     static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache), a.block_tables,
+                     a.query_start, a.context_lens, a.out, a.num_blocks, a.max_blocks, tiles, a.scale_log2);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_prefill_dt(int head_dim, int block_size, const PrefillArgs& a, hipStream_t stream) {
+  if (head_dim == 64)
+    return block_size == 16 ? launch_prefill_typed<DT, 64, 16>(a, stream) : launch_prefill_typed<DT, 64, 32>(a, stream);
+  return block_size == 16 ? launch_prefill_typed<DT, 128, 16>(a, stream) : launch_prefill_typed<DT, 128, 32>(a, stream);
+}
+
+}  // namespace
+
+int prefill_tile_queries() { return kTileQ; }
+
+hipError_t launch_prefill(int dtype, int head_dim, int block_size, const PrefillArgs& a, hipStream_t stream) {
+  switch (dtype) {
+    case PKV_F32: return launch_prefill_dt<PKV_F32>(head_dim, block_size, a, stream);
+    case PKV_F16: return launch_prefill_dt<PKV_F16>(head_dim, block_size, a, stream);
+    default: return launch_prefill_dt<PKV_BF16>(head_dim, block_size, a, stream);
+  }
+}
+
+}  // namespace pkv
