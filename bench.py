@@ -399,16 +399,101 @@ def continuous_batching(args):
     print(json.dumps(rec), flush=True)
 
 
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense matrix peaks, published
+
+
+def prefill(args):
+    """Prefill of a batch of prompts: the prompts' K/V are written into the paged cache (paged_kv_write),
+    then every prompt token attends causally over its sequence (paged_attention_prefill, MFMA)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_383_amd as pkv
+    import workloads as W
+    cfg = W.PrefillConfig()
+    dev = torch.device("cuda:0")
+    H, D, bs = cfg.num_heads, cfg.head_dim, cfg.block_size
+    es = elem_bytes(cfg.dtype)
+    dt = W.torch_dtype(cfg.dtype)
+    lens, nb, order = W.prefill_prompts(cfg)
+    pool = pkv.BlockPool(nb, bs, order)
+    for i, L in enumerate(lens.tolist()):
+        pool.allocate(i, L)
+    width = (cfg.max_len + bs - 1) // bs
+    tables, ctx = pool.build_tables(list(range(len(lens))), width)
+    T = int(lens.sum())
+    qs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    slots = np.concatenate([[tables[i][t // bs] * bs + t % bs for t in range(L)]
+                            for i, L in enumerate(lens.tolist())]).astype(np.int64)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    kc = torch.zeros((nb, H, bs, D), dtype=dt, device=dev)
+    vc = torch.zeros_like(kc)
+    kp = torch.randn((T, H, D), generator=gen, device=dev).to(dt)
+    vp = torch.randn((T, H, D), generator=gen, device=dev).to(dt)
+    q = torch.randn((T, H, D), generator=gen, device=dev).to(dt)
+    out = torch.empty_like(q)
+    t_tables, t_ctx = torch.from_numpy(tables).to(dev), torch.from_numpy(ctx).to(dev)
+    t_qs, t_slots = torch.from_numpy(qs).to(dev), torch.from_numpy(slots).to(dev)
+    maxq = int(lens.max())
+    # useful flops: each (query, key <= its position, head) pair costs 2 D for q.k and 2 D for p.v
+    pairs = int((lens * (lens + 1) // 2).sum())
+    flops = pairs * H * 4 * D
+    write_b = 2 * T * H * D * es * 2 + 8 * T
+
+    def step():
+        pkv.paged_kv_write(kp, vp, t_slots, kc, vc)
+        pkv.paged_attention_prefill(q, kc, vc, t_tables, t_qs, t_ctx, cfg.scale, maxq, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        pkv.paged_attention_prefill(q, kc, vc, t_tables, t_qs, t_ctx, cfg.scale, maxq, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    pre_us = a.elapsed_time(b) * 1e3 / args.steps
+    tflops = flops / pre_us / 1e6
+    peak = PEAK_MFMA_TFLOPS[cfg.dtype]
+    log(f"{cfg.name}: {T} tokens, {pairs} causal pairs; step {step_s * 1e6:.1f} us; prefill kernel {pre_us:.1f} us "
+        f"= {tflops:.1f} TFLOP/s ({tflops / peak:.1%} of {peak:.0f})")
+    rec = {
+        "metric": METRIC, "value": round(T / step_s, 1), "unit": "prompt tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "prompts": len(lens), "prompt_tokens": T, "num_heads": H, "head_dim": D,
+                   "block_size": bs, "step": "paged_kv_write(prompt K/V) + paged_attention_prefill",
+                   "flops_per_step": flops, "write_bytes_per_step": write_b},
+        "tokens_heads_per_s": round(T * H / step_s, 1),
+        "kernels_us": {"paged_attention_prefill": round(pre_us, 2)},
+        "roofline": {"kernel": "paged_attention_prefill (prefill_kernel)", "bound": "mfma",
+                     "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "mean_launch_us": round(pre_us, 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--workload", choices=["decode", "parallel_sampling", "continuous_batching"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "parallel_sampling", "continuous_batching", "prefill"],
+                    default="decode",
                     help="decode: one decode step of --config; parallel_sampling: a decode step over "
                          "prompts shared by parallel samples (copy-on-write copies + write + decode); "
-                         "continuous_batching: a many-step decode loop with admissions and releases")
+                         "continuous_batching: a many-step decode loop with admissions and releases; "
+                         "prefill: prompt K/V writes + causal paged prefill attention (MFMA)")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="split-context partition in tokens (0 = one pass); default: the library's choice")
     ap.add_argument("--rotate", type=int, default=None, help="independent input copies cycled over")
@@ -438,6 +523,9 @@ def main():
         return
     if args.workload == "continuous_batching":
         continuous_batching(args)
+        return
+    if args.workload == "prefill":
+        prefill(args)
         return
 
     dev = torch.device("cuda:0")

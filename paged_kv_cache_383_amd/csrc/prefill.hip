@@ -12,10 +12,11 @@
 //
 // Unlike decode, this is a dense contraction: a tile of queries meets every
 // key of a chunk, so the products go to MFMA.  Work decomposition: one
-// work-group of 4 wave64s per (head, 128-query tile, sequence); each wave owns
+// work-group of 8 wave64s per (head, 256-query tile, sequence); each wave owns
 // 32 queries as two 16-query sub-tiles.  Keys are walked in chunks of 32
 // (one 32-token block or two 16-token blocks), staged once per work-group in
-// LDS and shared by its 4 waves:
+// LDS and shared by its 8 waves (double-buffered: the next chunk's rows are
+// fetched into registers while this one is computed):
 //   K chunk as [key][d] (the cache's own row order),
 //   V chunk transposed as [d][key], so each lane's MFMA operand is a run of
 //   consecutive keys.
@@ -40,7 +41,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSub = 2;                        // 16-query sub-tiles per wave
 constexpr int kTileQ = kWaves * kSub * 16;     // queries per work-group
@@ -127,7 +128,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   constexpr int kEpv = 16 / kEs;                     // elements per 16-byte vector
   constexpr int kDSteps = D / M::kStep;              // MFMA k-steps over head_dim
   constexpr int kDTiles = D / 16;                    // 16-dim output tiles
-  __shared__ S sm;
+  constexpr int kBufs = 2 * sizeof(S) <= 48 * 1024 ? 2 : 1;   // fp32 head_dim 128 keeps one buffer
+  __shared__ S sm[kBufs];
   __shared__ int sm_bad;
 
   const int h = blockIdx.x;
@@ -195,58 +197,92 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   const int32_t* trow = block_tables + int64_t(s) * max_blocks;
   bool bad = false;
 
-  for (int c = 0; c < nchunks; ++c) {
+  // Software pipeline over chunks: chunk c + 1's K/V rows are fetched into
+  // registers while chunk c is computed from LDS; with two LDS buffers a
+  // single barrier per chunk orders the staging against the readers.
+  constexpr int kNv = (kVecs + kThreads - 1) / kThreads;   // 16-byte vectors per thread per tensor
+  u32x4 rk[kNv], rv[kNv];
+  auto fetch = [&](int c) {
     const int k0 = c * kChunk;
-    // Stage the chunk: K as [key][d], V transposed as [d][key]; keys past the
-    // context are zeros.
-    for (int v = threadIdx.x; v < kVecs; v += kThreads) {
+#pragma unroll
+    for (int i = 0; i < kNv; ++i) {
+      const int v = threadIdx.x + i * kThreads;
       const int key = v / kVpr, cv = v % kVpr;
       const int kg = k0 + key;
-      u32x4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (kg < L) {
+      rk[i] = u32x4{0, 0, 0, 0};
+      rv[i] = u32x4{0, 0, 0, 0};
+      if (v < kVecs && kg < L) {                     // keys past the context stay zero
         const int32_t b = trow[kg / BS];
         if (static_cast<uint64_t>(static_cast<int64_t>(b)) < static_cast<uint64_t>(num_blocks)) {
           const int64_t off = ((int64_t(b) * H + h) * BS + kg % BS) * int64_t(D * kEs) + cv * 16;
-          kk = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_cache + off));
-          vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_cache + off));
+          rk[i] = *reinterpret_cast<const u32x4*>(k_cache + off);
+          rv[i] = *reinterpret_cast<const u32x4*>(v_cache + off);
         } else {
           bad = true;
         }
       }
-      *reinterpret_cast<u32x4*>(&sm.k[key * S::kPitchK + cv * kEpv]) = kk;
-      const E* ve = reinterpret_cast<const E*>(&vv);
-#pragma unroll
-      for (int e = 0; e < kEpv; ++e) sm.vt[(cv * kEpv + e) * S::kPitchV + key] = ve[e];
     }
-    __syncthreads();
+  };
+  // K as [key][d], V transposed as [d][key].
+  auto stage = [&](S& buf) {
+#pragma unroll
+    for (int i = 0; i < kNv; ++i) {
+      const int v = threadIdx.x + i * kThreads;
+      if (v >= kVecs) continue;
+      const int key = v / kVpr, cv = v % kVpr;
+      *reinterpret_cast<u32x4*>(&buf.k[key * S::kPitchK + cv * kEpv]) = rk[i];
+      const E* ve = reinterpret_cast<const E*>(&rv[i]);
+#pragma unroll
+      for (int e = 0; e < kEpv; ++e) buf.vt[(cv * kEpv + e) * S::kPitchV + key] = ve[e];
+    }
+  };
 
+  fetch(0);
+  for (int c = 0; c < nchunks; ++c) {
+    const int k0 = c * kChunk;
+    S& sb = sm[c % kBufs];
+    if (kBufs == 1 && c > 0) __syncthreads();         // every wave is done reading the one buffer
+    stage(sb);
+    __syncthreads();
+    if (c + 1 < nchunks) fetch(c + 1);
+
+    // S^T for keys [k0, k0 + 32) as two 16-key tiles.  Each K fragment is read
+    // from LDS once and used for every sub-tile of the wave.
+    f32x4 st0[kSub], st1[kSub];
 #pragma unroll
     for (int u = 0; u < kSub; ++u) {
-      // S^T for keys [k0, k0 + 32): two 16-key tiles.
-      f32x4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
+      st0[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      st1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-      for (int st = 0; st < kDSteps; ++st) {
-        typename M::frag a0, a1;
-        if constexpr (M::kEpl == 1) {
-          a0 = sm.k[col * S::kPitchK + st * M::kStep + grp];
-          a1 = sm.k[(16 + col) * S::kPitchK + st * M::kStep + grp];
-        } else {
-          a0 = __builtin_bit_cast(typename M::frag,
-                                  *reinterpret_cast<const u32x4*>(&sm.k[col * S::kPitchK + st * M::kStep + grp * M::kEpl]));
-          a1 = __builtin_bit_cast(typename M::frag,
-                                  *reinterpret_cast<const u32x4*>(&sm.k[(16 + col) * S::kPitchK + st * M::kStep + grp * M::kEpl]));
-        }
-        st0 = M::mma(a0, qf[u][st], st0);
-        st1 = M::mma(a1, qf[u][st], st1);
+    for (int st = 0; st < kDSteps; ++st) {
+      typename M::frag a0, a1;
+      if constexpr (M::kEpl == 1) {
+        a0 = sb.k[col * S::kPitchK + st * M::kStep + grp];
+        a1 = sb.k[(16 + col) * S::kPitchK + st * M::kStep + grp];
+      } else {
+        a0 = __builtin_bit_cast(typename M::frag,
+                                *reinterpret_cast<const u32x4*>(&sb.k[col * S::kPitchK + st * M::kStep + grp * M::kEpl]));
+        a1 = __builtin_bit_cast(typename M::frag,
+                                *reinterpret_cast<const u32x4*>(&sb.k[(16 + col) * S::kPitchK + st * M::kStep + grp * M::kEpl]));
       }
-      // Scale, mask (key position > query position, or past the context), running max.
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) {
+        st0[u] = M::mma(a0, qf[u][st], st0[u]);
+        st1[u] = M::mma(a1, qf[u][st], st1[u]);
+      }
+    }
+    // Scale, mask (key position > query position), running max, P.
+    float p[kSub][8];
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
       float sc[8];
       float bm = kEmptyMax;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ka = k0 + 4 * grp + e, kb = k0 + 16 + 4 * grp + e;
-        sc[e] = ka <= qpos[u] ? st0[e] * scale_log2 : -__builtin_inff();
-        sc[4 + e] = kb <= qpos[u] ? st1[e] * scale_log2 : -__builtin_inff();
+        sc[e] = ka <= qpos[u] ? st0[u][e] * scale_log2 : -__builtin_inff();
+        sc[4 + e] = kb <= qpos[u] ? st1[u][e] * scale_log2 : -__builtin_inff();
         bm = fmaxf(bm, fmaxf(sc[e], sc[4 + e]));
       }
       bm = fmaxf(bm, __shfl_xor(bm, 16));
@@ -254,43 +290,46 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       const float m_new = fmaxf(m[u], bm);
       const float alpha = __builtin_amdgcn_exp2f(m[u] - m_new);
       m[u] = m_new;
-      float p[8];
       float ps = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(sc[e] - m_new);
-        ps += p[e];
+        p[u][e] = __builtin_amdgcn_exp2f(sc[e] - m_new);
+        ps += p[u][e];
       }
       l[u] = l[u] * alpha + ps;                      // this lane's share; groups summed at the end
 #pragma unroll
       for (int t = 0; t < kDTiles; ++t) acc[u][t] *= alpha;
-      // O^T += V^T P^T.
-      if constexpr (M::kEpl == 1) {
+    }
+    // O^T += V^T P^T; each V fragment is read once for all sub-tiles.
+    if constexpr (M::kEpl == 1) {
 #pragma unroll
-        for (int t = 0; t < kDTiles; ++t) {
-          const E* vrow = &sm.vt[(16 * t + col) * S::kPitchV];
+      for (int t = 0; t < kDTiles; ++t) {
+        const E* vrow = &sb.vt[(16 * t + col) * S::kPitchV];
 #pragma unroll
-          for (int half = 0; half < 2; ++half)
+        for (int half = 0; half < 2; ++half)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[u][t] = M::mma(vrow[16 * half + 4 * grp + e], p[4 * half + e], acc[u][t]);
-        }
-      } else {
-        typename M::frag pf;
+          for (int e = 0; e < 4; ++e) {
+            const E vv = vrow[16 * half + 4 * grp + e];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf[e] = M::from_f32(p[e]);
+            for (int u = 0; u < kSub; ++u) acc[u][t] = M::mma(vv, p[u][4 * half + e], acc[u][t]);
+          }
+      }
+    } else {
+      typename M::frag pf[kSub];
 #pragma unroll
-        for (int t = 0; t < kDTiles; ++t) {
-          const E* vrow = &sm.vt[(16 * t + col) * S::kPitchV];
-          typename M::frag vf;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * grp);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * grp);
-          vf = __builtin_bit_cast(typename M::frag, u32x4{lo.x, lo.y, hi.x, hi.y});
-          acc[u][t] = M::mma(vf, pf, acc[u][t]);
-        }
+      for (int u = 0; u < kSub; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[u][e] = M::from_f32(p[u][e]);
+#pragma unroll
+      for (int t = 0; t < kDTiles; ++t) {
+        const E* vrow = &sb.vt[(16 * t + col) * S::kPitchV];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * grp);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * grp);
+        const typename M::frag vf = __builtin_bit_cast(typename M::frag, u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+        for (int u = 0; u < kSub; ++u) acc[u][t] = M::mma(vf, pf[u], acc[u][t]);
       }
     }
-    __syncthreads();
   }
 
   if (bad) sm_bad = 1;

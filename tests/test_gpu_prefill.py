@@ -127,22 +127,22 @@ def test_prefill_full_size_llama13b_prompts(pkv):
 
 def test_prefill_contract(pkv, monkeypatch):
     rng = np.random.default_rng(520)
-    c = P.Case(rng, [200, 20], H=2, D=64, bs=16, dtype="f32")
-    qs = np.array([0, 200, 220], dtype=np.int32)
-    q = rng.standard_normal((220, 2, 64)).astype(np.float32)
+    c = P.Case(rng, [600, 20], H=2, D=64, bs=16, dtype="f32")
+    qs = np.array([0, 600, 620], dtype=np.int32)
+    q = rng.standard_normal((620, 2, 64)).astype(np.float32)
     args = (dev(q, "f32"), dev(c.k_pool, "f32"), dev(c.v_pool, "f32"), torch.from_numpy(c.tables).cuda(),
             torch.from_numpy(qs).cuda(), torch.from_numpy(c.context_lens).cuda(), c.scale)
-    good = pkv.paged_attention_prefill(*args, 200).cpu().numpy()
+    good = pkv.paged_attention_prefill(*args, 600).cpu().numpy()
     ref = oracle.prefill(q, c.k_pool, c.v_pool, c.tables, qs, c.context_lens, c.scale, 16, "f32")
     assert np.max(np.abs(good - ref)) <= 1e-5
-    # max_query_len 100 sizes the grid for one 128-query tile: sequence 0's 200 queries are not covered,
-    # so its rows are NaN; sequence 1 is untouched
+    # max_query_len 100 sizes the grid for one query tile, fewer than sequence 0's 600 queries: its rows
+    # are NaN; sequence 1 is untouched
     small = pkv.paged_attention_prefill(*args, 100).cpu().numpy()
-    assert np.all(np.isnan(small[:200])) and np.array_equal(small[200:], good[200:])
+    assert np.all(np.isnan(small[:600])) and np.array_equal(small[600:], good[600:])
     monkeypatch.setenv("PKV_DEBUG", "1")
     with pytest.raises(pkv.PagedKVError, match="max_query_len"):
         pkv.paged_attention_prefill(*args, 100)
     bad = c.context_lens.copy()
     bad[1] = 10                                            # fewer cached tokens than queries
     with pytest.raises(pkv.PagedKVError, match="context_lens"):
-        pkv.paged_attention_prefill(*args[:5], torch.from_numpy(bad).cuda(), c.scale, 200)
+        pkv.paged_attention_prefill(*args[:5], torch.from_numpy(bad).cuda(), c.scale, 600)

@@ -333,3 +333,33 @@ def batching_requests(cfg: BatchingConfig, n: int, seed: int | None = None):
                       cfg.prompt_min, cfg.prompt_max).astype(np.int64)
     gens = rng.integers(cfg.gen_min, cfg.gen_max + 1, n).astype(np.int64)
     return prompts, gens
+
+
+# ---------------------------------------------------------------- prefill
+
+@dataclass(frozen=True)
+class PrefillConfig:
+    """Prefill ("vLLM KV cache and PagedAttention explained", Step 6) of 16 prompts of U[128, 2048]
+    tokens at the LLaMA-2-13B layer shape: 40 heads, head_dim 128, 16-token blocks, bf16."""
+    name: str = "prefill_16_prompts_llama2_13b_layer_len128-2048_bf16"
+    prompts: int = 16
+    num_heads: int = 40
+    head_dim: int = 128
+    block_size: int = 16
+    dtype: str = BF16
+    min_len: int = 128
+    max_len: int = 2048
+    seed: int = SEED_BASE + 300
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+def prefill_prompts(cfg: PrefillConfig, seed: int | None = None):
+    """Prompt lengths, pool size (1.25x the blocks needed), a shuffled free order."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    lens = rng.integers(cfg.min_len, cfg.max_len + 1, cfg.prompts).astype(np.int64)
+    needed = int(((lens + cfg.block_size - 1) // cfg.block_size).sum())
+    nb = ceil_div(5 * needed, 4)
+    return lens, nb, rng.permutation(nb).astype(np.int32)
