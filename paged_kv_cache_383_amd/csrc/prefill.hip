@@ -18,8 +18,9 @@
 // LDS and shared by its 8 waves (double-buffered: the next chunk's rows are
 // fetched into registers while this one is computed):
 //   K chunk as [key][d] (the cache's own row order),
-//   V chunk transposed as [d][key], so each lane's MFMA operand is a run of
-//   consecutive keys.
+//   V chunk as [key][d] too, read as V^T with the transposing LDS load, so
+//   each lane's MFMA operand is a run of consecutive keys (fp32: stored
+//   transposed).
 // Per chunk and sub-tile a wave computes S^T = K Q^T with
 // v_mfma_f32_16x16x32_{bf16,f16} (fp32: 16x16x4), keeps each query's running
 // max across its four lane groups, and accumulates O^T += V^T P^T with P^T
@@ -103,15 +104,25 @@ __device__ __forceinline__ void store_out(void* base, int64_t i, float x) {
   }
 }
 
+// LDS staging of one 32-key chunk.  K keeps the cache's [key][d] order (a
+// 16-byte pad per row puts the 16 rows an MFMA operand read touches in
+// distinct banks).  For 16-bit types V keeps it too: the V^T operand is read
+// with the gfx950 transposing LDS load (ds_read_tr16_b64), which hands each
+// lane four consecutive keys of one dimension; a 32-byte pad per row spreads
+// the 16 keys one such read touches over the banks.  fp32 has no transposing
+// load: V is stored transposed, [d][key].
 template <int DT, int D>
 struct Smem {
   using E = elem_t<DT>;
-  static constexpr int kPadK = 16 / Mfma<DT>::kBytes;     // one 16-byte pad per K row
-  static constexpr int kPitchK = D + kPadK;
-  static constexpr int kPitchV = kChunk + 16 / Mfma<DT>::kBytes;
+  static constexpr bool kTr = Mfma<DT>::kBytes == 2;
+  static constexpr int kPitchK = D + 16 / Mfma<DT>::kBytes;
+  static constexpr int kPitchV = kTr ? D + 32 / Mfma<DT>::kBytes : kChunk + 16 / Mfma<DT>::kBytes;
   alignas(16) E k[kChunk * kPitchK];
-  alignas(16) E vt[D * kPitchV];
+  alignas(16) E v[kTr ? kChunk * kPitchV : D * kPitchV];
 };
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <int DT, int D, int BS>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(
@@ -231,9 +242,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       if (v >= kVecs) continue;
       const int key = v / kVpr, cv = v % kVpr;
       *reinterpret_cast<u32x4*>(&buf.k[key * S::kPitchK + cv * kEpv]) = rk[i];
-      const E* ve = reinterpret_cast<const E*>(&rv[i]);
+      if constexpr (S::kTr) {
+        *reinterpret_cast<u32x4*>(&buf.v[key * S::kPitchV + cv * kEpv]) = rv[i];
+      } else {
+        const E* ve = reinterpret_cast<const E*>(&rv[i]);
 #pragma unroll
-      for (int e = 0; e < kEpv; ++e) buf.vt[(cv * kEpv + e) * S::kPitchV + key] = ve[e];
+        for (int e = 0; e < kEpv; ++e) buf.v[(cv * kEpv + e) * S::kPitchV + key] = ve[e];
+      }
     }
   };
 
@@ -304,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     if constexpr (M::kEpl == 1) {
 #pragma unroll
       for (int t = 0; t < kDTiles; ++t) {
-        const E* vrow = &sb.vt[(16 * t + col) * S::kPitchV];
+        const E* vrow = &sb.v[(16 * t + col) * S::kPitchV];
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
@@ -320,12 +335,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       for (int u = 0; u < kSub; ++u)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pf[u][e] = M::from_f32(p[u][e]);
+      // Lane j of a 16-lane group points the transposing load at 4 dims of
+      // key 4g + j/4 (dims 16t + 4 (j % 4) ..); lane i then holds dim 16t + i
+      // of keys 4g .. 4g+3.  A second load does keys 16 + 4g .. 16 + 4g + 3.
+      const E* vbase = &sb.v[(4 * grp + col / 4) * S::kPitchV + 4 * (col % 4)];
 #pragma unroll
       for (int t = 0; t < kDTiles; ++t) {
-        const E* vrow = &sb.vt[(16 * t + col) * S::kPitchV];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * grp);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * grp);
-        const typename M::frag vf = __builtin_bit_cast(typename M::frag, u32x4{lo.x, lo.y, hi.x, hi.y});
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + 16 * t));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + 16 * S::kPitchV + 16 * t));
+        const typename M::frag vf = __builtin_bit_cast(
+            typename M::frag, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
         for (int u = 0; u < kSub; ++u) acc[u][t] = M::mma(vf, pf[u], acc[u][t]);
       }
