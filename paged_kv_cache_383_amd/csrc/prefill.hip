@@ -201,6 +201,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     for (int t = 0; t < kDTiles; ++t) acc[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  const int wave_first = first + q0 + wave * kSub * 16;      // position of the wave's first query
   // Keys this work-group needs: up to its last query's position.
   const int last_q = min(q0 + kTileQ, P) - 1;
   const int nkeys = first + last_q + 1;
@@ -213,8 +214,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   // single barrier per chunk orders the staging against the readers.
   constexpr int kNv = (kVecs + kThreads - 1) / kThreads;   // 16-byte vectors per thread per tensor
   u32x4 rk[kNv], rv[kNv];
+  const int nblocks = (L + BS - 1) / BS;
   auto fetch = [&](int c) {
     const int k0 = c * kChunk;
+    // The chunk's physical blocks (one or two), read once as wave-uniform values.
+    constexpr int kBlk = kChunk / BS;
+    int32_t bid[kBlk];
+#pragma unroll
+    for (int u = 0; u < kBlk; ++u) {
+      const int j = k0 / BS + u;
+      bid[u] = j < nblocks ? __builtin_amdgcn_readfirstlane(trow[j]) : 0;
+    }
 #pragma unroll
     for (int i = 0; i < kNv; ++i) {
       const int v = threadIdx.x + i * kThreads;
@@ -223,7 +233,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       rk[i] = u32x4{0, 0, 0, 0};
       rv[i] = u32x4{0, 0, 0, 0};
       if (v < kVecs && kg < L) {                     // keys past the context stay zero
-        const int32_t b = trow[kg / BS];
+        int32_t b = bid[0];
+#pragma unroll
+        for (int u = 1; u < kBlk; ++u)
+          if (key / BS == u) b = bid[u];
         if (static_cast<uint64_t>(static_cast<int64_t>(b)) < static_cast<uint64_t>(num_blocks)) {
           const int64_t off = ((int64_t(b) * H + h) * BS + kg % BS) * int64_t(D * kEs) + cv * 16;
           rk[i] = *reinterpret_cast<const u32x4*>(k_cache + off);
@@ -234,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       }
     }
   };
-  // K as [key][d], V transposed as [d][key].
+  // K as [key][d]; V as [key][d] (16-bit types) or transposed (fp32).
   auto stage = [&](S& buf) {
 #pragma unroll
     for (int i = 0; i < kNv; ++i) {
@@ -287,19 +300,30 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         st1[u] = M::mma(a1, qf[u][st], st1[u]);
       }
     }
-    // Scale, mask (key position > query position), running max, P.
+    // Scale, mask (key position > query position), running max, P.  Chunks
+    // wholly before the wave's first query need no mask.
+    const bool masked = k0 + kChunk - 1 > wave_first;
     float p[kSub][8];
 #pragma unroll
     for (int u = 0; u < kSub; ++u) {
       float sc[8];
       float bm = kEmptyMax;
+      if (masked) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ka = k0 + 4 * grp + e, kb = k0 + 16 + 4 * grp + e;
-        sc[e] = ka <= qpos[u] ? st0[u][e] * scale_log2 : -__builtin_inff();
-        sc[4 + e] = kb <= qpos[u] ? st1[u][e] * scale_log2 : -__builtin_inff();
-        bm = fmaxf(bm, fmaxf(sc[e], sc[4 + e]));
+        for (int e = 0; e < 4; ++e) {
+          const int ka = k0 + 4 * grp + e, kb = k0 + 16 + 4 * grp + e;
+          sc[e] = ka <= qpos[u] ? st0[u][e] * scale_log2 : -__builtin_inff();
+          sc[4 + e] = kb <= qpos[u] ? st1[u][e] * scale_log2 : -__builtin_inff();
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sc[e] = st0[u][e] * scale_log2;
+          sc[4 + e] = st1[u][e] * scale_log2;
+        }
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bm = fmaxf(bm, sc[e]);
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
       const float m_new = fmaxf(m[u], bm);
@@ -312,8 +336,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         ps += p[u][e];
       }
       l[u] = l[u] * alpha + ps;                      // this lane's share; groups summed at the end
+      if (__any(alpha != 1.f)) {                     // the running max moved for some query
 #pragma unroll
-      for (int t = 0; t < kDTiles; ++t) acc[u][t] *= alpha;
+        for (int t = 0; t < kDTiles; ++t) acc[u][t] *= alpha;
+      }
     }
     // O^T += V^T P^T; each V fragment is read once for all sub-tiles.
     if constexpr (M::kEpl == 1) {
