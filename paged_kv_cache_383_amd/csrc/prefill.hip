@@ -12,8 +12,10 @@
 //
 // Unlike decode, this is a dense contraction: a tile of queries meets every
 // key of a chunk, so the products go to MFMA.  Work decomposition: one
-// work-group of 8 wave64s per (head, 256-query tile, sequence); each wave owns
-// 32 queries as two 16-query sub-tiles.  Keys are walked in chunks of 32
+// work-group of 8 wave64s per (head, 128-query tile, sequence); each wave owns
+// 16 queries (kSub 16-query sub-tiles; one keeps the kernel at about 110
+// VGPRs, so two work-groups share a compute unit and hide each other's
+// latencies: 427 vs 328 TFLOP/s with two sub-tiles).  Keys are walked in chunks of 32
 // (one 32-token block or two 16-token blocks), staged once per work-group in
 // LDS and shared by its 8 waves (double-buffered: the next chunk's rows are
 // fetched into registers while this one is computed):
@@ -44,7 +46,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kSub = 2;                        // 16-query sub-tiles per wave
+constexpr int kSub = 1;                        // 16-query sub-tiles per wave
 constexpr int kTileQ = kWaves * kSub * 16;     // queries per work-group
 constexpr int kChunk = 32;                     // keys per chunk
 constexpr float kEmptyMax = -3.0e38f;
@@ -202,6 +204,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   }
 
   const int wave_first = first + q0 + wave * kSub * 16;      // position of the wave's first query
+  const int wave_q1 = min(q0 + (wave + 1) * kSub * 16, P);   // one past the wave's last query
+  const int wave_last = q0 + wave * kSub * 16 < P ? first + wave_q1 - 1 : -1;
   // Keys this work-group needs: up to its last query's position.
   const int last_q = min(q0 + kTileQ, P) - 1;
   const int nkeys = first + last_q + 1;
@@ -273,6 +277,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     stage(sb);
     __syncthreads();
     if (c + 1 < nchunks) fetch(c + 1);
+    // A wave skips chunks that start past its last query's position (every
+    // key would be masked); a wave without queries skips them all.  It still
+    // stages its share of every chunk for the other waves.
+    if (k0 > wave_last) continue;
 
     // S^T for keys [k0, k0 + 32) as two 16-key tiles.  Each K fragment is read
     // from LDS once and used for every sub-tile of the wave.
