@@ -36,7 +36,8 @@ def test_header_declares_the_two_calls():
     assert {"paged_kv_write", "paged_attention_decode", "paged_attention_workspace_bytes",
             "paged_attention_partition_size", "paged_kv_copy_blocks", "pkv_last_error", "pkv_pool_create",
             "pkv_pool_allocate", "pkv_pool_fork", "pkv_pool_append_slots", "pkv_pool_free",
-            "pkv_pool_build_tables"} <= set(fns)
+            "pkv_pool_build_tables", "paged_attention_prefill", "paged_kv_prepare_step", "pkv_batch_plan_step",
+            "pkv_pool_usage"} <= set(fns)
 
 
 def test_library_exports_every_declared_function(libpath):
@@ -61,6 +62,14 @@ def cp(**kw):
     a = dict(k=F, v=F, m=F, n=3, NB=64, H=4, D=64, bs=16, dt=0)
     a.update(kw)
     return lib.paged_kv_copy_blocks(a["k"], a["v"], a["m"], a["n"], a["NB"], a["H"], a["D"], a["bs"], a["dt"], None)
+lib.paged_attention_prefill.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i64,
+                                        ctypes.c_float, i32, vp, vp]
+def pf(**kw):
+    a = dict(q=F, k=F, v=F, tab=F, mb=128, qs=F, lens=F, B=16, mq=2048, H=40, D=128, bs=16, NB=5000,
+             scale=0.088, dt=2, out=F)
+    a.update(kw)
+    return lib.paged_attention_prefill(a["q"], a["k"], a["v"], a["tab"], a["mb"], a["qs"], a["lens"], a["B"],
+                                       a["mq"], a["H"], a["D"], a["bs"], a["NB"], a["scale"], a["dt"], a["out"], None)
 lib.paged_attention_workspace_bytes.argtypes = [i32] * 6
 lib.paged_attention_workspace_bytes.restype = sz
 lib.pkv_last_error.restype = ctypes.c_char_p
@@ -93,6 +102,10 @@ cases = [
   ("wr_head_dim", lambda: wr(D=80), 2), ("wr_block", lambda: wr(bs=64), 2),
   ("cp_neg", lambda: cp(n=-1), 1), ("cp_null", lambda: cp(m=None), 1), ("cp_zero", lambda: cp(n=0, k=None), 0),
   ("cp_dtype", lambda: cp(dt=9), 2), ("cp_blocks", lambda: cp(NB=0), 1),
+  ("pf_dtype", lambda: pf(dt=5), 2), ("pf_head_dim", lambda: pf(D=256), 2), ("pf_neg_seqs", lambda: pf(B=-1), 1),
+  ("pf_zero_seqs", lambda: pf(B=0, q=None), 0), ("pf_zero_q", lambda: pf(mq=0, q=None), 0),
+  ("pf_neg_q", lambda: pf(mq=-5), 1), ("pf_null_qs", lambda: pf(qs=None), 1),
+  ("pf_scale", lambda: pf(scale=float("nan")), 1), ("pf_grid", lambda: pf(mq=1 << 30), 2),
 ]
 for name, call, want in cases:
     got = call()

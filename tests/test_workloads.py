@@ -79,3 +79,21 @@ def test_poisoned_workload_on_cpu():
     free = np.nonzero(m.owner == W.FREE)[0]
     assert torch.isnan(k[torch.from_numpy(free)]).all()
     assert torch.isfinite(w.q).all() and torch.isfinite(w.k_new).all()
+
+
+def test_secondary_workloads_are_seeded_and_well_formed():
+    sc = W.SamplingConfig()
+    lens, nb, order = W.sampling_prompts(sc)
+    assert len(lens) == sc.prompts and lens.min() >= sc.min_len and lens.max() <= sc.max_len
+    assert sorted(order.tolist()) == list(range(nb))
+    assert nb >= -(-(lens.astype(np.int64) + 15) // 16).sum()
+    l2, _, o2 = W.sampling_prompts(sc)
+    assert np.array_equal(lens, l2) and np.array_equal(order, o2)
+    bc = W.BatchingConfig()
+    p, g = W.batching_requests(bc, 1000)
+    assert p.min() >= bc.prompt_min and p.max() <= bc.prompt_max and 300 < np.median(p) < 800
+    assert g.min() >= bc.gen_min and g.max() <= bc.gen_max
+    assert bc.width * bc.block_size >= bc.prompt_max + bc.gen_max
+    pc = W.PrefillConfig()
+    lens, nb, order = W.prefill_prompts(pc)
+    assert len(lens) == pc.prompts and nb == -(-5 * int(((lens + 15) // 16).sum()) // 4)
