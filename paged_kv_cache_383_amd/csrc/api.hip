@@ -222,7 +222,8 @@ extern "C" int paged_attention_prefill(const void* q, const void* k_cache, const
   if (num_seqs == 0 || max_query_len == 0) return ok();
   if (!q || !k_cache || !v_cache || !block_tables || !query_start || !context_lens || !out)
     return fail(PKV_EINVAL, "null pointer among q, k_cache, v_cache, block_tables, query_start, context_lens, out");
-  const int64_t tiles = (int64_t(max_query_len) + pkv::prefill_tile_queries() - 1) / pkv::prefill_tile_queries();
+  const int64_t tq = pkv::prefill_tile_queries(dtype);
+  const int64_t tiles = (int64_t(max_query_len) + tq - 1) / tq;
   if (num_heads > 65535 || num_seqs > 65535 || tiles > 65535)
     return fail(PKV_EUNSUPPORTED, "grid (%d heads, %lld query tiles, %d sequences) exceeds 65535", num_heads,
                 (long long)tiles, num_seqs);

@@ -88,7 +88,7 @@ struct PrefillArgs {
 };
 
 // Queries per prefill work-group (the grid's y extent is ceil(max_query_len / this)).
-int prefill_tile_queries();
+int prefill_tile_queries(int dtype);
 hipError_t launch_prefill(int dtype, int head_dim, int block_size, const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace pkv

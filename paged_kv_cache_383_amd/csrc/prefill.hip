@@ -404,13 +404,242 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   }
 }
 
+// 16-bit types: 32x32x16 MFMA tiles.  Each wave owns 32 queries (the columns
+// of a 32x32 S^T tile), so a K or V fragment read from LDS serves twice as
+// many queries as with 16-query tiles and a query's running max needs one
+// cross-lane step.  Layouts of v_mfma_f32_32x32x16: A[i][k] lane = i + 32
+// (k / 8), B[k][j] lane = j + 32 (k / 8), C[i][j] lane = j + 32 ((i / 4) % 2)
+// with element 4 (i / 8) + i % 4.  A lane of S^T therefore holds, for its query,
+// the keys 8 (e / 4) + 4 h + e % 4 (h = lane / 32, e < 16); the P^T operand of
+// k-step s is its elements 8 s .. 8 s + 7 as they are, and the V^T operand
+// lists the same keys in the same k-slot order (two transposing loads of four
+// keys each).
+constexpr int kWaves32 = 4;
+constexpr int kTileQ32 = 32 * kWaves32;
+constexpr float kLazy = 8.f;
+
+template <int DT, int D, int BS>
+__global__ __launch_bounds__(64 * kWaves32) __attribute__((amdgpu_waves_per_eu(3))) void prefill32_kernel(
+    const void* __restrict__ q, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ query_start,
+    const int32_t* __restrict__ context_lens, void* __restrict__ out, int64_t num_blocks, int32_t max_blocks,
+    int32_t tiles, float scale_log2) {
+  static_assert(Mfma<DT>::kBytes == 2, "16-bit types only");
+  using E = elem_t<DT>;
+  using S = Smem<DT, D>;
+  using frag = typename Mfma<DT>::frag;
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  constexpr int kT = 64 * kWaves32;
+  constexpr int kVpr = D * 2 / 16;                   // 16-byte vectors per K/V row
+  constexpr int kVecs = kChunk * kVpr;
+  constexpr int kNv = (kVecs + kT - 1) / kT;
+  constexpr int kDSteps = D / 16;                    // k-steps of S^T over head_dim
+  constexpr int kDTiles = D / 32;                    // 32-dim output tiles
+  __shared__ S sm[2];
+  __shared__ int sm_bad;
+
+  const int h = blockIdx.x;
+  const int tile = tiles - 1 - int(blockIdx.y);      // longest-running tiles first
+  const int s = blockIdx.z;
+  const int H = gridDim.x;
+  const int qa = query_start[s], qb = query_start[s + 1];
+  const int P = qb - qa;
+  const int L = context_lens[s];
+  const int q0 = tile * kTileQ32;
+  if (P <= 0 || q0 >= P) return;
+  const bool ok = P <= L && L <= max_blocks * BS && P <= tiles * kTileQ32;
+  const int first = L - P;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 31;                         // query of the wave (column of S^T)
+  const int hh = lane >> 5;                          // lane half
+  if (!ok) {
+    const int hi = tile == tiles - 1 ? P : min(q0 + kTileQ32, P);
+    for (int64_t i = threadIdx.x; i < int64_t(hi - q0) * D; i += kT)
+      store_out<DT>(out, (int64_t(qa + q0 + int(i / D)) * H + h) * D + i % D, __builtin_nanf(""));
+    return;
+  }
+  if (threadIdx.x == 0) sm_bad = 0;
+
+  const int qi = q0 + wave * 32 + col;
+  const int qpos = qi < P ? first + qi : -1;
+  frag qf[kDSteps];                                  // B operand: Q[col][16 st + 8 hh + e]
+  {
+    const E* qrow = static_cast<const E*>(q) + (int64_t(qa + (qi < P ? qi : 0)) * H + h) * D;
+#pragma unroll
+    for (int st = 0; st < kDSteps; ++st) {
+      const u32x4 raw = qi < P ? *reinterpret_cast<const u32x4*>(qrow + 16 * st + 8 * hh) : u32x4{0, 0, 0, 0};
+      qf[st] = __builtin_bit_cast(frag, raw);
+    }
+  }
+  f32x16 acc[kDTiles];
+#pragma unroll
+  for (int t = 0; t < kDTiles; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+  float m = kEmptyMax, l = 0.f;
+
+  const int wave_first = first + q0 + wave * 32;
+  const int wave_last = q0 + wave * 32 < P ? first + min(q0 + wave * 32 + 32, P) - 1 : -1;
+  const int last_q = min(q0 + kTileQ32, P) - 1;
+  const int nchunks = (first + last_q + 1 + kChunk - 1) / kChunk;
+  const int32_t* trow = block_tables + int64_t(s) * max_blocks;
+  const int nblocks = (L + BS - 1) / BS;
+  bool bad = false;
+
+  // Chunks start on block boundaries, so a thread's row within its block and
+  // its 16-byte column are the same for every chunk: only the block id moves.
+  const int64_t block_stride = int64_t(H) * BS * D * 2;
+  int64_t thread_off[kNv];
+#pragma unroll
+  for (int i = 0; i < kNv; ++i) {
+    const int v = threadIdx.x + i * kT;
+    thread_off[i] = (int64_t(h) * BS + (v / kVpr) % BS) * int64_t(D * 2) + (v % kVpr) * 16;
+  }
+  u32x4 rk[kNv], rv[kNv];
+  auto fetch = [&](int c) {
+    const int k0 = c * kChunk;
+    constexpr int kBlk = kChunk / BS;
+    int32_t bid[kBlk];
+#pragma unroll
+    for (int u = 0; u < kBlk; ++u) {
+      const int j = k0 / BS + u;
+      bid[u] = j < nblocks ? __builtin_amdgcn_readfirstlane(trow[j]) : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kNv; ++i) {
+      const int v = threadIdx.x + i * kT;
+      const int key = v / kVpr;
+      rk[i] = u32x4{0, 0, 0, 0};
+      rv[i] = u32x4{0, 0, 0, 0};
+      if (v < kVecs && k0 + key < L) {
+        int32_t b = bid[0];
+#pragma unroll
+        for (int u = 1; u < kBlk; ++u)
+          if (key / BS == u) b = bid[u];
+        if (static_cast<uint64_t>(static_cast<int64_t>(b)) < static_cast<uint64_t>(num_blocks)) {
+          const int64_t off = int64_t(b) * block_stride + thread_off[i];
+          rk[i] = *reinterpret_cast<const u32x4*>(k_cache + off);
+          rv[i] = *reinterpret_cast<const u32x4*>(v_cache + off);
+        } else {
+          bad = true;
+        }
+      }
+    }
+  };
+  auto stage = [&](S& buf) {
+#pragma unroll
+    for (int i = 0; i < kNv; ++i) {
+      const int v = threadIdx.x + i * kT;
+      if (v >= kVecs) continue;
+      const int key = v / kVpr, cv = v % kVpr;
+      *reinterpret_cast<u32x4*>(&buf.k[key * S::kPitchK + cv * 8]) = rk[i];
+      *reinterpret_cast<u32x4*>(&buf.v[key * S::kPitchV + cv * 8]) = rv[i];
+    }
+  };
+
+  fetch(0);
+  for (int c = 0; c < nchunks; ++c) {
+    const int k0 = c * kChunk;
+    S& sb = sm[c & 1];
+    stage(sb);
+    __syncthreads();
+    if (c + 1 < nchunks) fetch(c + 1);
+    if (k0 > wave_last) continue;
+
+    // S^T (32 keys x 32 queries).
+    f32x16 st;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st[e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < kDSteps; ++k) {
+      const frag a = __builtin_bit_cast(frag, *reinterpret_cast<const u32x4*>(&sb.k[col * S::kPitchK + 16 * k + 8 * hh]));
+      if constexpr (DT == PKV_BF16)
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[k], st, 0, 0, 0);
+      else
+        st = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[k], st, 0, 0, 0);
+    }
+    // Scale, mask, running max (in-lane over 16 keys, then across the lane halves).
+    float sc[16];
+    float bm = kEmptyMax;
+    if (k0 + kChunk - 1 > wave_first) {
+      const int lim = qpos - k0 - 4 * hh;            // key k0 + 8 (e/4) + 4 hh + e%4 <= qpos
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[e] = 8 * (e / 4) + e % 4 <= lim ? st[e] * scale_log2 : -__builtin_inff();
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[e] = st[e] * scale_log2;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) bm = fmaxf(bm, sc[e]);
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    // The reference max moves only when the chunk's max exceeds it by more
+    // than kLazy (base-2 units): until then p <= 2^kLazy, harmless in fp32 and
+    // in the 16-bit P operand, and the softmax is the same for any reference.
+    const float m_new = bm > m + kLazy ? bm : m;
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    frag pf[2];
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pe = __builtin_amdgcn_exp2f(sc[e] - m_new);
+      ps += pe;
+      pf[e / 8][e % 8] = Mfma<DT>::from_f32(pe);
+    }
+    l = l * alpha + ps;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int t = 0; t < kDTiles; ++t) acc[t] *= alpha;
+    }
+    // O^T += V^T P^T: per 32-dim tile, two k-steps of 16 keys; lane group G
+    // (16 lanes) points the transposing load at key 16 s + 4 hh (+ 8) + j / 4,
+    // dims 32 t + 16 (G % 2) + 4 (j % 4).
+    const int grp16 = (lane >> 4) & 1;
+    const E* vbase = &sb.v[(4 * hh + (lane & 15) / 4) * S::kPitchV + 16 * grp16 + 4 * (lane & 3)];
+#pragma unroll
+    for (int t = 0; t < kDTiles; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const E* p0 = vbase + (16 * ks) * S::kPitchV + 32 * t;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * S::kPitchV));
+        const frag vf = __builtin_bit_cast(
+            frag, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        if constexpr (DT == PKV_BF16)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], acc[t], 0, 0, 0);
+        else
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[ks], acc[t], 0, 0, 0);
+      }
+  }
+
+  if (bad) sm_bad = 1;
+  __syncthreads();
+  float lt = l + __shfl_xor(l, 32);
+  if (qi >= P) return;
+  const float inv = sm_bad ? __builtin_nanf("") : 1.f / lt;
+  const int64_t base = (int64_t(qa + qi) * H + h) * D;
+#pragma unroll
+  for (int t = 0; t < kDTiles; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) store_out<DT>(out, base + 32 * t + 8 * (e / 4) + 4 * hh + e % 4, acc[t][e] * inv);
+}
+
 template <int DT, int D, int BS>
 hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
-  const int tiles = (a.max_query_len + kTileQ - 1) / kTileQ;
-  const dim3 grid(unsigned(a.num_heads), unsigned(tiles), unsigned(a.num_seqs));
-  hipLaunchKernelGGL((prefill_kernel<DT, D, BS>), grid, dim3(kThreads), 0, stream, a.q,
-                     static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache), a.block_tables,
-                     a.query_start, a.context_lens, a.out, a.num_blocks, a.max_blocks, tiles, a.scale_log2);
+  if constexpr (DT == PKV_F32) {
+    const int tiles = (a.max_query_len + kTileQ - 1) / kTileQ;
+    const dim3 grid(unsigned(a.num_heads), unsigned(tiles), unsigned(a.num_seqs));
+    hipLaunchKernelGGL((prefill_kernel<DT, D, BS>), grid, dim3(kThreads), 0, stream, a.q,
+                       static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache), a.block_tables,
+                       a.query_start, a.context_lens, a.out, a.num_blocks, a.max_blocks, tiles, a.scale_log2);
+  } else {
+    const int tiles = (a.max_query_len + kTileQ32 - 1) / kTileQ32;
+    const dim3 grid(unsigned(a.num_heads), unsigned(tiles), unsigned(a.num_seqs));
+    hipLaunchKernelGGL((prefill32_kernel<DT, D, BS>), grid, dim3(64 * kWaves32), 0, stream, a.q,
+                       static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache), a.block_tables,
+                       a.query_start, a.context_lens, a.out, a.num_blocks, a.max_blocks, tiles, a.scale_log2);
+  }
   return hipGetLastError();
 }
 
@@ -423,7 +652,7 @@ hipError_t launch_prefill_dt(int head_dim, int block_size, const PrefillArgs& a,
 
 }  // namespace
 
-int prefill_tile_queries() { return kTileQ; }
+int prefill_tile_queries(int dtype) { return dtype == PKV_F32 ? kTileQ : kTileQ32; }
 
 hipError_t launch_prefill(int dtype, int head_dim, int block_size, const PrefillArgs& a, hipStream_t stream) {
   switch (dtype) {
