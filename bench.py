@@ -1,24 +1,27 @@
-"""Decode-step benchmark on one MI355X: slot-mapping write + paged attention.
+"""Decode-step benchmark on one MI355X: slot-mapping append + paged attention.
 
-A step is one pass of the whole path over one batch: paged_kv_write of each
-sequence's newest token into its cache slot, then paged_attention_decode of
-one query per sequence over its paged K/V.  The default workload is the
-LLaMA-2-13B-shaped single-layer batch (64 sequences, 40 heads, head_dim 128,
-block 16, bf16, contexts uniform in [128, 2048], pool 1.25x the needed blocks
-in a shuffled free list).  Inputs are resident in HBM before timing starts;
-consecutive steps rotate over independent copies of the inputs (each larger
-than the 256 MB Infinity Cache) so no step reads data the previous one left
-in the caches.
+A step is one pass of the whole path over one batch: each sequence's newest
+token's K/V goes into its cache slot, then one query per sequence attends over
+its paged K/V.  By default the step is the library's fused call,
+paged_attention_decode_step (append and attention in one launch); with
+--two-call-step it is paged_kv_write + paged_attention_decode (both forms are
+timed and reported).  The default workload is the LLaMA-2-13B-shaped
+single-layer batch (64 sequences, 40 heads, head_dim 128, block 16, bf16,
+contexts uniform in [128, 2048], pool 1.25x the needed blocks in a shuffled
+free list).  Inputs are resident in HBM before timing starts; consecutive steps
+rotate over independent copies of the inputs (each larger than the 256 MB
+Infinity Cache) so no step reads data the previous one left in the caches.
 
 Prints one JSON line:
-  value          algorithmic GB/s of the whole step (write + decode bytes / step time)
+  value          algorithmic GB/s of the whole step (append + decode bytes / step time)
   roofline       the decode call (the partition kernel, plus the LSE reduce when the
                  context is split), algorithmic bytes per launch / its mean duration from
                  HIP events on the launch stream, vs the 8 TB/s HBM peak
   cpu_baseline   the float64 CPU oracle on a bounded sample of the same workload
 Timing: the K steps run back to back with no event between them (wall clock and one HIP event
-pair bracket them); then the decode call alone and the write alone run K times back to back, each
-bracketed by a HIP event pair, for the per-launch averages.
+pair bracket them); then the other form of the step, the decode call alone and the write alone
+run K times back to back, each bracketed by a HIP event pair, for the per-launch averages.
+Other workloads (--workload): parallel_sampling, continuous_batching, prefill.
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--config 2]
 """
 from __future__ import annotations
@@ -498,6 +501,9 @@ def main():
                     help="split-context partition in tokens (0 = one pass); default: the library's choice")
     ap.add_argument("--rotate", type=int, default=None, help="independent input copies cycled over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--two-call-step", action="store_true",
+                    help="time the decode step as paged_kv_write + paged_attention_decode instead of the fused "
+                         "paged_attention_decode_step")
     ap.add_argument("--copy-calibration", type=int, default=None, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -555,25 +561,44 @@ def main():
         pkv.paged_attention_decode(s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens, cfg.scale,
                                    out=outs[i % rotate], workspace=ws, partition_size=part)
 
-    for i in range(args.warmup):
+    def fused_step(i):
+        s = sets[i % rotate]
+        pkv.paged_attention_decode_step(s.q, s.k_new, s.v_new, s.k_cache, s.v_cache, s.block_tables,
+                                        s.context_lens, cfg.scale, out=outs[i % rotate], workspace=ws,
+                                        partition_size=part)
+
+    def two_call_step(i):
         write(i)
         decode(i)
+
+    step = two_call_step if args.two_call_step else fused_step
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
-    # Timed region 1: whole steps (write + decode), no per-step events (an event record between
-    # kernels adds several microseconds of queue work); wall clock and a HIP event pair around it.
+    # Timed region 1: whole steps, no per-step events (an event record between kernels adds several
+    # microseconds of queue work); wall clock and a HIP event pair around it.  A step is the library's
+    # decode step (paged_attention_decode_step: the newest tokens' append and the attention in one
+    # launch), or with --two-call-step paged_kv_write + paged_attention_decode.
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
     for i in range(args.steps):
-        write(i)
-        decode(i)
+        step(i)
     ev1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
     step_ev_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    # the other form of the step, for comparison
+    other = fused_step if args.two_call_step else two_call_step
+    ev0.record()
+    for i in range(args.steps):
+        other(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    other_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
 
     # Timed region 2: the dominant kernel alone, launched back to back over the rotating inputs on the
     # stream the library launches on (torch's current stream); average launch duration from a HIP
@@ -593,7 +618,8 @@ def main():
     torch.cuda.synchronize()
     write_us = ev2.elapsed_time(ev3) * 1e3 / args.steps
     achieved = nbytes["decode"] / (decode_us * 1e-6) / 1e9
-    log(f"step {step_s * 1e6:.1f} us (wall; {step_ev_us:.1f} us by events), decode {decode_us:.1f} us, "
+    log(f"step {step_s * 1e6:.1f} us (wall; {step_ev_us:.1f} us by events; "
+        f"{'fused' if args.two_call_step else 'two-call'} step {other_us:.1f} us), decode {decode_us:.1f} us, "
         f"write {write_us:.1f} us -> decode {achieved:.0f} GB/s = {achieved / PEAK_HBM_GBS:.1%} of peak")
 
     cpu = None
@@ -627,13 +653,16 @@ def main():
             "pool_blocks": meta.num_blocks,
             "partition_size": resolved,
             "partition_choice": "library (PKV_PARTITION_AUTO)" if part == pkv.PARTITION_AUTO else "caller",
-            "step": "paged_kv_write(one new token per sequence) + paged_attention_decode",
+            "step": ("paged_kv_write(one new token per sequence) + paged_attention_decode" if args.two_call_step
+                     else "paged_attention_decode_step (append of one new token per sequence + attention, "
+                          "one launch)"),
             "step_algorithmic_bytes": nbytes["step"],
         },
         "tokens_heads_per_s": round(th / step_s, 1),
         "fraction_of_peak": round(nbytes["step"] / step_s / 1e9 / PEAK_HBM_GBS, 4),
         "kernels_us": {"paged_kv_write": round(write_us, 2), "paged_attention_decode": round(decode_us, 2),
-                       "step_by_events": round(step_ev_us, 2)},
+                       "step_by_events": round(step_ev_us, 2),
+                       ("paged_attention_decode_step" if args.two_call_step else "two_call_step"): round(other_us, 2)},
         "roofline": {
             "kernel": "paged_attention_decode (decode_partition_kernel" + (" + lse_reduce_kernel)" if resolved else ")"),
             "bound": "hbm",

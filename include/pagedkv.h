@@ -235,6 +235,29 @@ int paged_kv_prepare_step(int32_t* block_tables, int32_t max_blocks_per_seq, int
                           const int32_t* updates, int64_t num_updates, const int32_t* new_lens,
                           int64_t* slot_mapping, int32_t block_size, int64_t num_blocks, void* stream);
 
+/*
+ * paged_attention_decode_step -- one decode step in one launch: the append of
+ * each sequence's newest token and the attention over its cache.  Equivalent to
+ * paged_kv_write of k_new[i], v_new[i] into the slot of position L - 1
+ * (block_tables[i, (L-1) / block_size] * block_size + (L-1) % block_size, with
+ * L = context_lens[i] the length after the append; [explain] Step 6: the decode
+ * token's K/V goes to the next slot of its last block) followed by
+ * paged_attention_decode with the same arguments: same results, bit for bit.
+ * Within the launch, the work-group of each (sequence, head) that covers
+ * position L - 1 stores that row before reading the block.  Rows with L = 0
+ * append nothing and are zero.
+ *
+ *   k_new, v_new  [num_seqs, num_heads, head_dim], dtype, read
+ *   k_cache,
+ *   v_cache       written at the newest slots, read everywhere else
+ * Other arguments, ownership and errors as for paged_attention_decode.
+ */
+int paged_attention_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                int32_t block_size, int64_t num_blocks, float scale, int32_t dtype, void* out,
+                                void* workspace, size_t workspace_bytes, int32_t partition_size, void* stream);
+
 /* Text of the calling thread's last non-OK status (empty string if none). */
 const char* pkv_last_error(void);
 

@@ -13,6 +13,8 @@ If the library is not built, every call raises.
                                     max_blocks_per_seq, block_size, partition_size)
     paged_attention_partition_size(num_seqs, num_heads, max_blocks_per_seq, block_size,
                                    partition_size)
+    paged_attention_decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                                out=None, workspace=None, partition_size=PARTITION_AUTO)
     paged_attention_prefill(q, k_cache, v_cache, block_tables, query_start, context_lens, scale,
                             max_query_len, out=None)
     paged_kv_copy_blocks(k_cache, v_cache, block_mapping)
@@ -78,6 +80,8 @@ def lib() -> ctypes.CDLL:
             "pkv_pool_num_tokens": ([vp, i64], i64), "pkv_pool_table": ([vp, i64, vp, i64], i64),
             "pkv_pool_free_list": ([vp, vp, i64], i64),
             "pkv_pool_usage": ([vp, vp], ctypes.c_int),
+            "paged_attention_decode_step": ([vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i64,
+                                             ctypes.c_float, i32, vp, vp, sz, i32, vp], ctypes.c_int),
             "paged_attention_prefill": ([vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i64,
                                          ctypes.c_float, i32, vp, vp], ctypes.c_int),
             "pkv_batch_create": ([vp, i32, i32], vp), "pkv_batch_destroy": ([vp], None),
@@ -193,6 +197,46 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
                                             bs, NB, float(scale), _dtype_code(q), out.data_ptr(),
                                             workspace.data_ptr(), ws_bytes, partition_size,
                                             _stream(q.device)))
+    return out
+
+
+def paged_attention_decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out=None,
+                                workspace=None, partition_size=DEFAULT_PARTITION):
+    """One decode step in one launch: k_new[i], v_new[i] go to the slot of position context_lens[i] - 1,
+    then paged attention as paged_attention_decode (bit-identical to the two calls)."""
+    import torch
+    _device_tensor("q", q, k_cache.dtype, 3)
+    _device_tensor("k_new", k_new, k_cache.dtype, 3)
+    _device_tensor("v_new", v_new, k_cache.dtype, 3)
+    _device_tensor("k_cache", k_cache, None, 4)
+    _device_tensor("v_cache", v_cache, k_cache.dtype, 4)
+    _device_tensor("block_tables", block_tables, torch.int32, 2)
+    _device_tensor("context_lens", context_lens, torch.int32, 1)
+    NB, H, bs, D = k_cache.shape
+    B = q.shape[0]
+    if v_cache.shape != k_cache.shape or q.shape[1:] != (H, D) or k_new.shape != q.shape or v_new.shape != q.shape:
+        raise ValueError("q, k_new, v_new [B, H, D] and caches [NB, H, bs, D] do not match")
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _device_tensor("out", out, q.dtype, 3)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    M = block_tables.shape[1]
+    need = paged_attention_workspace_bytes(B, H, D, M, bs, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _device_tensor("workspace", workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        _check(lib().paged_attention_decode_step(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                                 k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), M,
+                                                 context_lens.data_ptr(), B, H, D, bs, NB, float(scale),
+                                                 _dtype_code(q), out.data_ptr(), workspace.data_ptr(), ws_bytes,
+                                                 partition_size, _stream(q.device)))
     return out
 
 

@@ -270,12 +270,15 @@ extern "C" int paged_attention_prefill(const void* q, const void* k_cache, const
   return ok();
 }
 
-extern "C" int paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
-                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                      const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                                      float scale, int32_t dtype, void* out, void* workspace,
-                                      size_t workspace_bytes, int32_t partition_size, void* stream) {
+namespace {
+
+// Decode, optionally with the newest tokens' K/V appended first (k_new, v_new
+// non-null: the fused step).
+int decode_common(const void* q, const void* k_new, const void* v_new, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                  int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                  float scale, int32_t dtype, void* out, void* workspace, size_t workspace_bytes,
+                  int32_t partition_size, void* stream) {
   if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs must be >= 0 (got %d)", num_seqs);
   if (int rc = check_shape(dtype, num_heads, head_dim, block_size, num_blocks)) return rc;
   if (max_blocks_per_seq <= 0)
@@ -290,6 +293,7 @@ extern "C" int paged_attention_decode(const void* q, const void* k_cache, const 
   if (num_seqs == 0) return ok();
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return fail(PKV_EINVAL, "null pointer among q, k_cache, v_cache, block_tables, context_lens, out");
+  if ((k_new == nullptr) != (v_new == nullptr)) return fail(PKV_EINVAL, "k_new and v_new must both be given");
   if (num_heads > 65535 || num_seqs > 65535)
     return fail(PKV_EUNSUPPORTED, "num_heads %d / num_seqs %d exceed the grid limit 65535", num_heads, num_seqs);
   const int32_t pb = part_blocks_for(max_blocks_per_seq, block_size, partition_size);
@@ -321,8 +325,10 @@ extern "C" int paged_attention_decode(const void* q, const void* k_cache, const 
   }
   pkv::DecodeArgs a{};
   a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
+  a.k_cache = const_cast<void*>(k_cache);          // written only when k_new is given
+  a.v_cache = const_cast<void*>(v_cache);
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.out = out;
@@ -340,4 +346,29 @@ extern "C" int paged_attention_decode(const void* q, const void* k_cache, const 
   hipError_t e = pkv::launch_decode(dtype, head_dim, block_size, a, st);
   if (e != hipSuccess) return hip_fail(e, "paged_attention_decode launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" int paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                      float scale, int32_t dtype, void* out, void* workspace,
+                                      size_t workspace_bytes, int32_t partition_size, void* stream) {
+  return decode_common(q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_heads, head_dim, block_size, num_blocks, scale, dtype, out, workspace,
+                       workspace_bytes, partition_size, stream);
+}
+
+extern "C" int paged_attention_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                           void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                           int32_t dtype, void* out, void* workspace, size_t workspace_bytes,
+                                           int32_t partition_size, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return fail(PKV_EINVAL, "null k_new or v_new");
+  return decode_common(q, k_new, v_new, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_heads, head_dim, block_size, num_blocks, scale, dtype, out, workspace,
+                       workspace_bytes, partition_size, stream);
 }

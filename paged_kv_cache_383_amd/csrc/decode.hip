@@ -205,11 +205,11 @@ __device__ __forceinline__ bool context_ok(int32_t L, int32_t cap) { return L >=
 
 template <int DT, int D, int BS, int WAVES, int TPS, int NST>
 __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
-    const void* __restrict__ q, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
+    const void* __restrict__ q, char* __restrict__ k_cache, char* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     void* __restrict__ out, float* __restrict__ ws_m, float* __restrict__ ws_l,
     float* __restrict__ ws_acc, int64_t num_blocks, int32_t max_blocks, int32_t part_blocks,
-    int32_t partitions, float scale_log2) {
+    int32_t partitions, float scale_log2, const char* __restrict__ k_new, const char* __restrict__ v_new) {
   using G = Geo<DT, D, BS, WAVES>;
   constexpr int kWaves = WAVES;
   const int h = blockIdx.x;
@@ -228,6 +228,30 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
   if (p >= parts) return;
   const int j0 = p * part_blocks;
   const int j1 = min(j0 + part_blocks, nb);
+
+  // Decode step with the append fused in (k_new given): the work-group whose
+  // partition holds the newest token, position L - 1, first stores that
+  // token's K and V rows of its head into their slot ("vLLM KV cache and
+  // PagedAttention explained", Step 6: the decode token's K/V goes to the next
+  // slot of the sequence's last block), waits for the stores, and only then
+  // lets its waves read the block.
+  if (k_new != nullptr && p == parts - 1) {
+    const int32_t bl = block_tables[int64_t(s) * max_blocks + (L - 1) / BS];
+    if (static_cast<uint64_t>(static_cast<int64_t>(bl)) < static_cast<uint64_t>(num_blocks)) {
+      constexpr int kVecRow = G::kRowBytes / 16;
+      const int64_t dst = ((int64_t(bl) * gridDim.x + blockIdx.x) * BS + (L - 1) % BS) * G::kRowBytes;
+      const int64_t src = row * G::kRowBytes;
+      const int i = threadIdx.x;
+      if (i < kVecRow) {
+        *reinterpret_cast<u32x4*>(k_cache + dst + 16 * i) = *reinterpret_cast<const u32x4*>(k_new + src + 16 * i);
+      } else if (i < 2 * kVecRow) {
+        const int c = i - kVecRow;
+        *reinterpret_cast<u32x4*>(v_cache + dst + 16 * c) = *reinterpret_cast<const u32x4*>(v_new + src + 16 * c);
+      }
+      __builtin_amdgcn_s_waitcnt(0);                 // the stores have reached the L2 the loads read
+    }
+    __syncthreads();
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -423,9 +447,10 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   constexpr int kWaves = waves_for<BS>();
   constexpr int kTps = tiles_for<DT, D, BS>();
   hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, kWaves, kTps, stages_for<DT, kTps>()>), grid, dim3(64 * kWaves), 0, stream, a.q,
-                     static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
+                     static_cast<char*>(a.k_cache), static_cast<char*>(a.v_cache),
                      a.block_tables, a.context_lens, a.out, a.ws_m, a.ws_l, a.ws_acc, a.num_blocks,
-                     a.max_blocks, a.part_blocks, a.partitions, a.scale_log2);
+                     a.max_blocks, a.part_blocks, a.partitions, a.scale_log2,
+                     static_cast<const char*>(a.k_new), static_cast<const char*>(a.v_new));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.partitions <= 1) return e;
   hipLaunchKernelGGL((lse_reduce_kernel<DT, D>), dim3(unsigned(a.num_heads), unsigned(a.num_seqs)),

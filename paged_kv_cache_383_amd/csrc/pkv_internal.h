@@ -39,8 +39,10 @@ inline WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_heads, int
 
 struct DecodeArgs {
   const void* q;
-  const void* k_cache;
-  const void* v_cache;
+  void* k_cache;                 // written only by the fused step (k_new != nullptr)
+  void* v_cache;
+  const void* k_new;             // [B, H, D] newest tokens' K/V for the fused step, or nullptr
+  const void* v_new;
   const int32_t* block_tables;
   const int32_t* context_lens;
   void* out;

@@ -37,7 +37,7 @@ def test_header_declares_the_two_calls():
             "paged_attention_partition_size", "paged_kv_copy_blocks", "pkv_last_error", "pkv_pool_create",
             "pkv_pool_allocate", "pkv_pool_fork", "pkv_pool_append_slots", "pkv_pool_free",
             "pkv_pool_build_tables", "paged_attention_prefill", "paged_kv_prepare_step", "pkv_batch_plan_step",
-            "pkv_pool_usage"} <= set(fns)
+            "pkv_pool_usage", "paged_attention_decode_step"} <= set(fns)
 
 
 def test_library_exports_every_declared_function(libpath):

@@ -125,6 +125,32 @@ def test_decode_step_matches_oracle(pkv, cfg_id):
         assert np.max(np.abs(got)) <= vmax * (1 + 1e-2)
 
 
+@pytest.mark.parametrize("cfg_id", sorted(W.CONFIGS))
+def test_fused_decode_step_equals_write_then_decode(pkv, cfg_id):
+    """paged_attention_decode_step (append fused into the decode launch) against paged_kv_write +
+    paged_attention_decode: caches and outputs bit for bit, at each configuration's full size, with the
+    library's split and with 512-token partitions."""
+    meta = W.make_metadata(cfg_id)
+    cfg = meta.cfg
+    say(f"[fused] config {cfg_id} {cfg.name}")
+    for part in (pkv.PARTITION_AUTO, 512):
+        a = W.make_workload(meta, "cuda")
+        b = W.make_workload(meta, "cuda")
+        pkv.paged_kv_write(a.k_new, a.v_new, a.slot_mapping, a.k_cache, a.v_cache)
+        out_a = pkv.paged_attention_decode(a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, cfg.scale,
+                                           partition_size=part)
+        out_b = pkv.paged_attention_decode_step(b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.block_tables,
+                                                b.context_lens, cfg.scale, partition_size=part)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a.view(torch.int16 if out_a.element_size() == 2 else torch.int32),
+                           out_b.view(torch.int16 if out_b.element_size() == 2 else torch.int32)), part
+        for x, y in ((a.k_cache, b.k_cache), (a.v_cache, b.v_cache)):
+            vi = torch.int16 if x.element_size() == 2 else torch.int32
+            assert torch.equal(x.view(vi), y.view(vi))
+        del a, b
+        torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ small cases: every shape and edge
 
 SHAPES = [(dt, D, bs) for dt in ("f32", "f16", "bf16") for D in (64, 128) for bs in (16, 32)]
