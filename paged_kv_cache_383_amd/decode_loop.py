@@ -11,10 +11,11 @@ Per step the host side is the library's C++ block pool and batch planner
 (pkv_batch_plan_step): it reserves each running row's new slot, copying a
 shared last block when needed, and lists the device block-table entries that
 changed.  The plan goes to the GPU in one asynchronous copy from pinned memory,
-then five kernels run in stream order: the prompt writes of newly admitted
+then the kernels run in stream order: the prompt writes of newly admitted
 requests (paged_kv_write), paged_kv_prepare_step (table updates, context
-lengths and the slot mapping, on the device), paged_kv_copy_blocks,
-paged_kv_write of the new tokens, and paged_attention_decode.  Nothing waits
+lengths and the slot mapping, on the device), paged_kv_copy_blocks, and
+paged_attention_decode_step (the new tokens' append and the attention, one
+launch).  Nothing waits
 for the GPU unless the host runs two steps ahead of it.  This module only
 marshals: which request comes next is the caller's choice.
 """
@@ -22,7 +23,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (BlockPool, Batch, paged_attention_decode, paged_kv_copy_blocks, paged_kv_prepare_step,
+from . import (BlockPool, Batch, paged_attention_decode_step, paged_kv_copy_blocks, paged_kv_prepare_step,
                paged_kv_write)
 
 
@@ -134,9 +135,8 @@ class DecodeLoop:
                               d[:self.rows], self.slots, self.block_size, self.num_blocks)
         if len(copies):
             paged_kv_copy_blocks(self.k_cache, self.v_cache, d[o_cp:o_pr].view(torch.int64).view(-1, 2))
-        paged_kv_write(k_new, v_new, self.slots, self.k_cache, self.v_cache)
-        out = paged_attention_decode(q, self.k_cache, self.v_cache, self.tables, self.lens, self.scale, out=out,
-                                     workspace=self.workspace)
+        out = paged_attention_decode_step(q, k_new, v_new, self.k_cache, self.v_cache, self.tables, self.lens,
+                                          self.scale, out=out, workspace=self.workspace)
         self.last_copies = copies.copy()
         self.last_lens = lens.copy()
         self.last_prompt_tokens = n_prompt
