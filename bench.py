@@ -476,7 +476,7 @@ def prefill(args):
                    "flops_per_step": flops, "write_bytes_per_step": write_b},
         "tokens_heads_per_s": round(T * H / step_s, 1),
         "kernels_us": {"paged_attention_prefill": round(pre_us, 2)},
-        "roofline": {"kernel": "paged_attention_prefill (prefill_kernel)", "bound": "mfma",
+        "roofline": {"kernel": "paged_attention_prefill (prefill32_kernel: 32x32x16 MFMA tiles)", "bound": "mfma",
                      "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": None,
                      "algorithmic_flops_per_launch": flops, "mean_launch_us": round(pre_us, 2)},

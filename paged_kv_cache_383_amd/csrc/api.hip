@@ -227,6 +227,12 @@ extern "C" int paged_attention_prefill(const void* q, const void* k_cache, const
   if (num_heads > 65535 || num_seqs > 65535 || tiles > 65535)
     return fail(PKV_EUNSUPPORTED, "grid (%d heads, %lld query tiles, %d sequences) exceeds 65535", num_heads,
                 (long long)tiles, num_seqs);
+  // 16-bit types launch one 256-thread work-group per (sequence, head, tile),
+  // (sequence, head) pairs rounded up to a multiple of 8, in a 1-D grid whose
+  // size in threads must fit 32 bits.
+  if (dtype != PKV_F32 && ((int64_t(num_heads) * num_seqs + 7) / 8 * 8) * tiles * 256 > int64_t(UINT32_MAX))
+    return fail(PKV_EUNSUPPORTED, "grid of %d heads x %d sequences x %lld query tiles is too large", num_heads,
+                num_seqs, (long long)tiles);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (debug_checks()) {
     std::vector<int32_t> qs(size_t(num_seqs) + 1), lens(num_seqs), tab(size_t(num_seqs) * max_blocks_per_seq);

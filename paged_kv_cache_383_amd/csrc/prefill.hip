@@ -11,11 +11,14 @@
 // 무엇이 달라지는가").
 //
 // Unlike decode, this is a dense contraction: a tile of queries meets every
-// key of a chunk, so the products go to MFMA.  Work decomposition: one
-// work-group of 8 wave64s per (head, 128-query tile, sequence); each wave owns
-// 16 queries (kSub 16-query sub-tiles; one keeps the kernel at about 110
-// VGPRs, so two work-groups share a compute unit and hide each other's
-// latencies: 427 vs 328 TFLOP/s with two sub-tiles).  Keys are walked in chunks of 32
+// key of a chunk, so the products go to MFMA.  Two kernels share the chunk
+// walk and the LDS staging.  bf16/f16 take prefill32_kernel (32x32x16 tiles,
+// described above it): 4 wave64s per (head, 128-query tile, sequence), 32
+// queries per wave.  fp32 takes prefill_kernel (16x16x4 tiles), described
+// here: one work-group of 8 wave64s per (head, 128-query tile, sequence); each
+// wave owns 16 queries (kSub 16-query sub-tiles; one keeps the kernel at about
+// 110 VGPRs, so two work-groups share a compute unit and hide each other's
+// latencies).  Keys are walked in chunks of 32
 // (one 32-token block or two 16-token blocks), staged once per work-group in
 // LDS and shared by its 8 waves (double-buffered: the next chunk's rows are
 // fetched into registers while this one is computed):
@@ -50,6 +53,8 @@ constexpr int kSub = 1;                        // 16-query sub-tiles per wave
 constexpr int kTileQ = kWaves * kSub * 16;     // queries per work-group
 constexpr int kChunk = 32;                     // keys per chunk
 constexpr float kEmptyMax = -3.0e38f;
+// Word 3 of a gfx9 raw buffer resource: 32-bit data format, no swizzle.
+constexpr int kBufferWord3 = 0x00020000;
 
 template <int DT>
 struct Mfma;
@@ -413,35 +418,105 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 // the keys 8 (e / 4) + 4 h + e % 4 (h = lane / 32, e < 16); the P^T operand of
 // k-step s is its elements 8 s .. 8 s + 7 as they are, and the V^T operand
 // lists the same keys in the same k-slot order (two transposing loads of four
-// keys each).
+// keys each).  K/V chunks reach LDS by loads that write it directly (no
+// register staging), three buffers deep: chunk c + 2 is in flight while c is
+// computed, and a chunk costs one barrier.
 constexpr int kWaves32 = 4;
 constexpr int kTileQ32 = 32 * kWaves32;
+// Work order (one work-group per (sequence, head, 128-query tile)).  Work-
+// groups go to the 8 XCDs round robin by linear id, and the tiles of one
+// (sequence, head) read the same K/V chunks from position 0 up, so they are
+// placed on one XCD back to back, where they run together and share its L2;
+// measured ~8 % faster than launching every sequence's last tiles first.
+// For balance the tiles are split into kBands bands (longest tiles first):
+// band 0 of every (sequence, head) is launched before band 1, and so on, so
+// that the longest tiles never start last.
+constexpr int kBands = 3;
 constexpr float kLazy = 8.f;
+
+// x of lane i and of lane i ^ 32, in every lane, by the gfx950 cross-half
+// lane swap (no round trip through LDS): swapping the upper half of one copy
+// of x with the lower half of another leaves the lower halves' values in the
+// first result and the upper halves' in the second.
+struct Halves {
+  float lo, hi;
+};
+__device__ inline Halves halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// 16-byte buffer load straight into LDS: lane i's 16 bytes land at LDS byte
+// address lds + 16 i; bytes at or past nrec read as zero.  base, nrec and lds
+// must be wave-uniform.  Written as inline assembly so that the compiler's
+// wait-count insertion, which cannot tell which LDS buffer such a load
+// writes, does not hold LDS reads of the other buffers behind it; the caller
+// waits for completion itself (vmcnt, then a barrier).  The compiler does not
+// see the instruction inside, so the asm supplies the wait states the gfx9
+// hazard rules ask for before it: one after an SALU write of M0 (the LDS
+// address) and five after a VALU write (v_readfirstlane) of an SGPR of the
+// buffer descriptor.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ inline void load_lds16(const char* base, int nrec, uint32_t voff, uint32_t lds) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const i32x4 desc = {__builtin_amdgcn_readfirstlane(int(uint32_t(a))),
+                      __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffff)),
+                      __builtin_amdgcn_readfirstlane(nrec), kBufferWord3};
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(desc), "{m0}"(lds) : "memory");
+}
+__device__ inline uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>((uintptr_t)(__attribute__((address_space(3))) const void*)p);
+}
 
 template <int DT, int D, int BS>
 __global__ __launch_bounds__(64 * kWaves32) __attribute__((amdgpu_waves_per_eu(3))) void prefill32_kernel(
     const void* __restrict__ q, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ query_start,
     const int32_t* __restrict__ context_lens, void* __restrict__ out, int64_t num_blocks, int32_t max_blocks,
-    int32_t tiles, float scale_log2) {
+    int32_t tiles, float scale_log2, int32_t num_heads, int32_t num_seqs) {
   static_assert(Mfma<DT>::kBytes == 2, "16-bit types only");
   using E = elem_t<DT>;
-  using S = Smem<DT, D>;
   using frag = typename Mfma<DT>::frag;
   typedef float f32x16 __attribute__((ext_vector_type(16)));
   constexpr int kT = 64 * kWaves32;
-  constexpr int kVpr = D * 2 / 16;                   // 16-byte vectors per K/V row
-  constexpr int kVecs = kChunk * kVpr;
-  constexpr int kNv = (kVecs + kT - 1) / kT;
+  constexpr int kVpr = D * 2 / 16;                   // 16-byte columns per K/V row
+  constexpr int kRowsPerLoad = 64 / kVpr;            // rows one wave-wide 16-byte load fills
+  constexpr int kNl = kChunk / kRowsPerLoad / kWaves32;  // such loads per wave per tensor per chunk
   constexpr int kDSteps = D / 16;                    // k-steps of S^T over head_dim
   constexpr int kDTiles = D / 32;                    // 32-dim output tiles
-  __shared__ S sm[2];
+  static_assert(kNl * kWaves32 * kRowsPerLoad == kChunk && BS % kRowsPerLoad == 0, "load tiling");
+  // Three chunk buffers (K and V rows, [key][d], no padding; 16-byte columns
+  // swizzled against bank conflicts, see below), filled by loads that write
+  // LDS directly: two chunks are in flight while a third is computed.
+  __shared__ __attribute__((aligned(16))) E lk0[kChunk * D], lv0[kChunk * D];
+  __shared__ __attribute__((aligned(16))) E lk1[kChunk * D], lv1[kChunk * D];
+  __shared__ __attribute__((aligned(16))) E lk2[kChunk * D], lv2[kChunk * D];
   __shared__ int sm_bad;
 
-  const int h = blockIdx.x;
-  const int tile = tiles - 1 - int(blockIdx.y);      // longest-running tiles first
-  const int s = blockIdx.z;
-  const int H = gridDim.x;
+  // Linear id n: XCD x = n % 8 takes (sequence, head) pairs x, x + 8, ...
+  // (pair = sequence * H + head); its r-th work-group (r = n / 8) is, in band
+  // order, tile k of the band of its local pair r / w (w = the band's tile
+  // count), tiles counted from the last (longest) one.
+  const int H = num_heads;
+  int h, s, tile;
+  {
+    const int n = blockIdx.x, x = n % 8;
+    int r = n / 8;
+    const int J = (num_heads * num_seqs + 7) / 8;      // pairs per XCD (rounded up)
+    int b = 0, klo = 0, khi = tiles / kBands;
+    while (r >= J * (khi - klo)) {
+      r -= J * (khi - klo);
+      ++b;
+      klo = khi;
+      khi = (b + 1) * tiles / kBands;
+    }
+    const int w = khi - klo;
+    const int pr = (r / w) * 8 + x;
+    if (pr >= num_heads * num_seqs) return;
+    s = pr / num_heads;
+    h = pr % num_heads;
+    tile = tiles - 1 - (klo + r % w);
+  }
   const int qa = query_start[s], qb = query_start[s + 1];
   const int P = qb - qa;
   const int L = context_lens[s];
@@ -464,14 +539,6 @@ __global__ __launch_bounds__(64 * kWaves32) __attribute__((amdgpu_waves_per_eu(3
   const int qi = q0 + wave * 32 + col;
   const int qpos = qi < P ? first + qi : -1;
   frag qf[kDSteps];                                  // B operand: Q[col][16 st + 8 hh + e]
-  {
-    const E* qrow = static_cast<const E*>(q) + (int64_t(qa + (qi < P ? qi : 0)) * H + h) * D;
-#pragma unroll
-    for (int st = 0; st < kDSteps; ++st) {
-      const u32x4 raw = qi < P ? *reinterpret_cast<const u32x4*>(qrow + 16 * st + 8 * hh) : u32x4{0, 0, 0, 0};
-      qf[st] = __builtin_bit_cast(frag, raw);
-    }
-  }
   f32x16 acc[kDTiles];
 #pragma unroll
   for (int t = 0; t < kDTiles; ++t)
@@ -484,95 +551,107 @@ __global__ __launch_bounds__(64 * kWaves32) __attribute__((amdgpu_waves_per_eu(3
   const int last_q = min(q0 + kTileQ32, P) - 1;
   const int nchunks = (first + last_q + 1 + kChunk - 1) / kChunk;
   const int32_t* trow = block_tables + int64_t(s) * max_blocks;
-  const int nblocks = (L + BS - 1) / BS;
   bool bad = false;
 
-  // Chunks start on block boundaries, so a thread's row within its block and
-  // its 16-byte column are the same for every chunk: only the block id moves.
-  const int64_t block_stride = int64_t(H) * BS * D * 2;
-  int64_t thread_off[kNv];
+  // Swizzle (LDS of 64 four-byte banks, one 256-byte bank row holding
+  // kRb = 128 / D chunk rows): 16-byte column c of chunk row r sits at
+  // column c ^ (b % kVpr) in K and c ^ 4 (b % (kVpr / 4)) in V, b = r / kRb.
+  // The S^T operand read (16 lanes: 16 rows, one column) and the transposing
+  // V^T read (32 lanes: 4 rows, 4 columns, 2 halves) then touch distinct
+  // banks.  Wave w loads rows 8 w .. 8 w + 7 of each chunk (one
+  // block: blocks hold 16 or 32 rows), kRowsPerLoad rows per wave-wide load:
+  // lane i writes 16 bytes at LDS offset 16 i of the load's rows (the
+  // load-to-LDS layout) and therefore fetches the logical column whose
+  // swizzled position that is.  Chunks start on block boundaries, so a
+  // lane's offset within its block is the same for every chunk.
+  constexpr int kRowsPerWave = kChunk / kWaves32;
+  constexpr int kRb = 128 / D;                       // chunk rows per 256-byte bank row
+  static_assert(kRowsPerWave == kNl * kRowsPerLoad && BS % kRowsPerWave == 0, "a wave loads within one block");
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t koff[kNl], voff[kNl];
 #pragma unroll
-  for (int i = 0; i < kNv; ++i) {
-    const int v = threadIdx.x + i * kT;
-    thread_off[i] = (int64_t(h) * BS + (v / kVpr) % BS) * int64_t(D * 2) + (v % kVpr) * 16;
+  for (int i = 0; i < kNl; ++i) {
+    const int r = wave_s * kRowsPerWave + i * kRowsPerLoad + lane / kVpr;
+    const int pc = lane % kVpr;
+    const int b = r / kRb;
+    koff[i] = uint32_t((r % BS) * D * 2 + (pc ^ (b % kVpr)) * 16);
+    voff[i] = uint32_t((r % BS) * D * 2 + (pc ^ (4 * (b % (kVpr / 4)))) * 16);
   }
-  u32x4 rk[kNv], rv[kNv];
-  auto fetch = [&](int c) {
-    const int k0 = c * kChunk;
-    constexpr int kBlk = kChunk / BS;
-    int32_t bid[kBlk];
-#pragma unroll
-    for (int u = 0; u < kBlk; ++u) {
-      const int j = k0 / BS + u;
-      bid[u] = j < nblocks ? __builtin_amdgcn_readfirstlane(trow[j]) : 0;
-    }
-#pragma unroll
-    for (int i = 0; i < kNv; ++i) {
-      const int v = threadIdx.x + i * kT;
-      const int key = v / kVpr;
-      rk[i] = u32x4{0, 0, 0, 0};
-      rv[i] = u32x4{0, 0, 0, 0};
-      if (v < kVecs && k0 + key < L) {
-        int32_t b = bid[0];
-#pragma unroll
-        for (int u = 1; u < kBlk; ++u)
-          if (key / BS == u) b = bid[u];
-        if (static_cast<uint64_t>(static_cast<int64_t>(b)) < static_cast<uint64_t>(num_blocks)) {
-          const int64_t off = int64_t(b) * block_stride + thread_off[i];
-          rk[i] = *reinterpret_cast<const u32x4*>(k_cache + off);
-          rv[i] = *reinterpret_cast<const u32x4*>(v_cache + off);
-        } else {
-          bad = true;
-        }
-      }
-    }
+  const int64_t block_stride = int64_t(H) * BS * D * 2;
+  const char* kh = k_cache + int64_t(h) * BS * D * 2;
+  const char* vh = v_cache + int64_t(h) * BS * D * 2;
+  const uint32_t nb32 = uint32_t(min<int64_t>(num_blocks, INT32_MAX));
+  constexpr int kBlk = kChunk / BS;
+  const int ublk = wave_s * kRowsPerWave / BS;       // the wave's block within a chunk
+  // Block id of the wave's rows of chunk c (0 past the context).
+  auto block_of = [&](int c) -> int32_t {
+    const int j = c * kBlk + ublk;
+    return j * BS < L ? __builtin_amdgcn_readfirstlane(trow[j]) : 0;
   };
-  auto stage = [&](S& buf) {
+  auto issue = [&](int c, int32_t b, E* dk, E* dv) {
+    const int j = c * kBlk + ublk;
+    const int rows = min(max(L - j * BS, 0), BS);
+    const bool in = uint32_t(b) < nb32;
+    if (rows > 0 && !in) bad = true;
+    const int64_t off = in ? int64_t(b) * block_stride : 0;
+    const int n = in ? rows * D * 2 : 0;             // rows past the context read as zero
 #pragma unroll
-    for (int i = 0; i < kNv; ++i) {
-      const int v = threadIdx.x + i * kT;
-      if (v >= kVecs) continue;
-      const int key = v / kVpr, cv = v % kVpr;
-      *reinterpret_cast<u32x4*>(&buf.k[key * S::kPitchK + cv * 8]) = rk[i];
-      *reinterpret_cast<u32x4*>(&buf.v[key * S::kPitchV + cv * 8]) = rv[i];
+    for (int i = 0; i < kNl; ++i) {
+      const int r0 = wave_s * kRowsPerWave + i * kRowsPerLoad;
+      load_lds16(kh + off, n, koff[i], lds_address(dk + r0 * D));
+      load_lds16(vh + off, n, voff[i], lds_address(dv + r0 * D));
     }
   };
 
-  fetch(0);
-  for (int c = 0; c < nchunks; ++c) {
-    const int k0 = c * kChunk;
-    S& sb = sm[c & 1];
-    stage(sb);
-    __syncthreads();
-    if (c + 1 < nchunks) fetch(c + 1);
-    if (k0 > wave_last) continue;
+  // Reader addresses (elements).  S^T operand of k-step k: row col, logical
+  // column 2 k + hh.  V^T operand of tile t, k-step ks: lane j of its 16-lane
+  // group G reads 4 keys from row r = 16 ks + 4 hh + j / 4 (+8) at dims
+  // 32 t + 16 (G % 2) + 4 (j % 4): logical column 4 t + a, a = 2 (G % 2) +
+  // (j % 4) / 2, swizzled to 4 (t ^ q) + a, where q = (r / kRb) % (kVpr / 4)
+  // depends on j (and hh) only: 16 ks + 8 and 4 hh add whole multiples.
+  int ka[kDSteps];
+#pragma unroll
+  for (int k = 0; k < kDSteps; ++k) ka[k] = col * D + 8 * ((2 * k + hh) ^ ((col / kRb) % kVpr));
+  const int j16 = lane & 15;
+  const int vr = 4 * hh + j16 / 4;
+  const int qv = (vr / kRb) % (kVpr / 4);
+  const int av = 2 * ((lane >> 4) & 1) + (j16 % 4) / 2;
+  int vb[kDTiles];
+#pragma unroll
+  for (int t = 0; t < kDTiles; ++t) vb[t] = vr * D + 8 * (4 * (t ^ qv) + av) + 4 * (j16 % 2);
 
+  auto compute = [&](int c, const E* sk, const E* sv) {
+    const int k0 = c * kChunk;
     // S^T (32 keys x 32 queries).
     f32x16 st;
 #pragma unroll
     for (int e = 0; e < 16; ++e) st[e] = 0.f;
 #pragma unroll
     for (int k = 0; k < kDSteps; ++k) {
-      const frag a = __builtin_bit_cast(frag, *reinterpret_cast<const u32x4*>(&sb.k[col * S::kPitchK + 16 * k + 8 * hh]));
+      const frag a = __builtin_bit_cast(frag, *reinterpret_cast<const u32x4*>(sk + ka[k]));
       if constexpr (DT == PKV_BF16)
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[k], st, 0, 0, 0);
       else
         st = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[k], st, 0, 0, 0);
     }
-    // Scale, mask, running max (in-lane over 16 keys, then across the lane halves).
+    // Mask, running max (in-lane over 16 keys, then across the lane halves).
+    // The scale (> 0) keeps the order of scores, so the max is taken on the
+    // raw products and the scale enters once per key, in the exponent's fma.
     float sc[16];
-    float bm = kEmptyMax;
     if (k0 + kChunk - 1 > wave_first) {
       const int lim = qpos - k0 - 4 * hh;            // key k0 + 8 (e/4) + 4 hh + e%4 <= qpos
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sc[e] = 8 * (e / 4) + e % 4 <= lim ? st[e] * scale_log2 : -__builtin_inff();
+      for (int e = 0; e < 16; ++e) sc[e] = 8 * (e / 4) + e % 4 <= lim ? st[e] : -__builtin_inff();
     } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sc[e] = st[e] * scale_log2;
+      for (int e = 0; e < 16; ++e) sc[e] = st[e];
     }
+    float rmax = sc[0];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) bm = fmaxf(bm, sc[e]);
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    for (int e = 1; e < 16; ++e) rmax = fmaxf(rmax, sc[e]);
+    const Halves hm = halves(rmax);
+    rmax = fmaxf(hm.lo, hm.hi);
+    const float bm = fmaxf(rmax * scale_log2, kEmptyMax);
     // The reference max moves only when the chunk's max exceeds it by more
     // than kLazy (base-2 units): until then p <= 2^kLazy, harmless in fp32 and
     // in the 16-bit P operand, and the softmax is the same for any reference.
@@ -583,7 +662,7 @@ __global__ __launch_bounds__(64 * kWaves32) __attribute__((amdgpu_waves_per_eu(3
     float ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(sc[e] - m_new);
+      const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], scale_log2, -m_new));
       ps += pe;
       pf[e / 8][e % 8] = Mfma<DT>::from_f32(pe);
     }
@@ -592,18 +671,14 @@ __global__ __launch_bounds__(64 * kWaves32) __attribute__((amdgpu_waves_per_eu(3
 #pragma unroll
       for (int t = 0; t < kDTiles; ++t) acc[t] *= alpha;
     }
-    // O^T += V^T P^T: per 32-dim tile, two k-steps of 16 keys; lane group G
-    // (16 lanes) points the transposing load at key 16 s + 4 hh (+ 8) + j / 4,
-    // dims 32 t + 16 (G % 2) + 4 (j % 4).
-    const int grp16 = (lane >> 4) & 1;
-    const E* vbase = &sb.v[(4 * hh + (lane & 15) / 4) * S::kPitchV + 16 * grp16 + 4 * (lane & 3)];
+    // O^T += V^T P^T: per 32-dim tile, two k-steps of 16 keys.
 #pragma unroll
     for (int t = 0; t < kDTiles; ++t)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const E* p0 = vbase + (16 * ks) * S::kPitchV + 32 * t;
+        const E* p0 = sv + vb[t] + 16 * ks * D;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * S::kPitchV));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * D));
         const frag vf = __builtin_bit_cast(
             frag, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
         if constexpr (DT == PKV_BF16)
@@ -611,11 +686,53 @@ __global__ __launch_bounds__(64 * kWaves32) __attribute__((amdgpu_waves_per_eu(3
         else
           acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[ks], acc[t], 0, 0, 0);
       }
+  };
+
+  // Chunk c: wait for this wave's loads of chunk c (those of chunk c + 1 may
+  // still be in flight), barrier (every wave's loads of c have landed and
+  // every wave is done with chunk c - 1), start chunk c + 2 into the buffer
+  // chunk c - 1 used, then compute.
+  constexpr int kWaitOne = (2 * kNl) | (7 << 4) | (15 << 8);  // vmcnt(2 kNl), other counters free
+  constexpr int kWaitAll = (7 << 4) | (15 << 8);              // vmcnt(0)
+  // The block id of chunk c + 2 is read before the wait and the barrier,
+  // which hide its latency; no scalar load is then in flight during the
+  // compute (its LDS reads could only wait for all outstanding LDS and
+  // scalar loads together).
+  auto step = [&](int c, const E* sk, const E* sv, E* nk, E* nv) {
+    const int32_t b = c + 2 < nchunks ? block_of(c + 2) : 0;
+    if (c + 1 < nchunks)
+      __builtin_amdgcn_s_waitcnt(kWaitOne);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __builtin_amdgcn_s_barrier();
+    if (c + 2 < nchunks) issue(c + 2, b, nk, nv);
+    if (c * kChunk <= wave_last) compute(c, sk, sv);
+  };
+  // Chunk 0's loads, then the query fragments, then a full wait: both are
+  // needed first, and the compiler's own count of outstanding loads (it does
+  // not see the loads to LDS) is then zero, so it adds no waits of its own
+  // inside the loop.
+  issue(0, block_of(0), lk0, lv0);
+  {
+    const E* qrow = static_cast<const E*>(q) + (int64_t(qa + (qi < P ? qi : 0)) * H + h) * D;
+#pragma unroll
+    for (int st = 0; st < kDSteps; ++st) {
+      const u32x4 raw = qi < P ? *reinterpret_cast<const u32x4*>(qrow + 16 * st + 8 * hh) : u32x4{0, 0, 0, 0};
+      qf[st] = __builtin_bit_cast(frag, raw);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  if (nchunks > 1) issue(1, block_of(1), lk1, lv1);
+  for (int c = 0; c < nchunks; c += 3) {
+    step(c, lk0, lv0, lk2, lv2);
+    if (c + 1 < nchunks) step(c + 1, lk1, lv1, lk0, lv0);
+    if (c + 2 < nchunks) step(c + 2, lk2, lv2, lk1, lv1);
   }
 
   if (bad) sm_bad = 1;
   __syncthreads();
-  float lt = l + __shfl_xor(l, 32);
+  const Halves hl = halves(l);
+  const float lt = hl.lo + hl.hi;
   if (qi >= P) return;
   const float inv = sm_bad ? __builtin_nanf("") : 1.f / lt;
   const int64_t base = (int64_t(qa + qi) * H + h) * D;
@@ -635,10 +752,12 @@ hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
                        a.query_start, a.context_lens, a.out, a.num_blocks, a.max_blocks, tiles, a.scale_log2);
   } else {
     const int tiles = (a.max_query_len + kTileQ32 - 1) / kTileQ32;
-    const dim3 grid(unsigned(a.num_heads), unsigned(tiles), unsigned(a.num_seqs));
+    const int64_t pairs8 = (int64_t(a.num_heads) * a.num_seqs + 7) / 8 * 8;
+    const dim3 grid(unsigned(pairs8 * tiles));
     hipLaunchKernelGGL((prefill32_kernel<DT, D, BS>), grid, dim3(64 * kWaves32), 0, stream, a.q,
                        static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache), a.block_tables,
-                       a.query_start, a.context_lens, a.out, a.num_blocks, a.max_blocks, tiles, a.scale_log2);
+                       a.query_start, a.context_lens, a.out, a.num_blocks, a.max_blocks, tiles, a.scale_log2,
+                       a.num_heads, a.num_seqs);
   }
   return hipGetLastError();
 }
