@@ -11,10 +11,11 @@
 // 무엇이 달라지는가").
 //
 // Unlike decode, this is a dense contraction: a tile of queries meets every
-// key of a chunk, so the products go to MFMA.  Two kernels share the chunk
-// walk and the LDS staging.  bf16/f16 take prefill32_kernel (32x32x16 tiles,
-// described above it): 4 wave64s per (head, 128-query tile, sequence), 32
-// queries per wave.  fp32 takes prefill_kernel (16x16x4 tiles), described
+// key of a chunk, so the products go to MFMA.  Both kernels walk the keys in
+// 32-key chunks staged in LDS.  bf16/f16 take prefill32_kernel (32x32x16
+// tiles, K/V loaded straight into LDS; described above it): 4 wave64s per
+// (sequence, head, 128-query tile), 32 queries per wave.  fp32 takes
+// prefill_kernel (16x16x4 tiles), described
 // here: one work-group of 8 wave64s per (head, 128-query tile, sequence); each
 // wave owns 16 queries (kSub 16-query sub-tiles; one keeps the kernel at about
 // 110 VGPRs, so two work-groups share a compute unit and hide each other's
