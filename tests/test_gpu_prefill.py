@@ -131,6 +131,56 @@ def test_prefill_full_size_llama13b_prompts(pkv):
         assert torch.equal(again.view(torch.int16), out.view(torch.int16))
 
 
+SCALE_SHAPES = [("f16", 64, 32), ("bf16", 128, 32), ("f16", 128, 16)]
+
+
+@pytest.mark.parametrize("dt,D,bs", SCALE_SHAPES, ids=[f"{a}-d{b}-bs{c}" for a, b, c in SCALE_SHAPES])
+def test_prefill_long_prompts_other_shapes(pkv, dt, D, bs):
+    """Long prompts (many 32-key chunks per work-group, several query tiles, one sequence behind an 800-token
+    cached prefix) at the 16-bit shapes the full-size test does not cover: sampled rows against the oracle's
+    decode of each row's query over its prefix, and every row through run-to-run equality."""
+    rng = np.random.default_rng(530 + D + bs)
+    H = 8
+    lens = np.array([2100, 1500, 900])
+    news = np.array([2100, 700, 900])                    # sequence 1 keeps an 800-token prefix
+    cfg = W.Config(5, f"prefill_{dt}_d{D}_bs{bs}", 3, H, D, bs, dt, 1.0, 4096, 512)   # pool rule of config 5
+    meta = W.make_metadata(cfg, lens=lens, seed=531)
+    w = W.make_workload(meta, "cuda")
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    T = int(lens.sum())
+    slots = np.concatenate([[meta.block_tables[i][t // bs] * bs + t % bs for t in range(L)]
+                            for i, L in enumerate(lens)]).astype(np.int64)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(532)
+    kp = torch.randn((T, H, D), generator=gen, device="cuda").to(tdt)
+    vp = torch.randn((T, H, D), generator=gen, device="cuda").to(tdt)
+    pkv.paged_kv_write(kp, vp, torch.from_numpy(slots).cuda(), w.k_cache, w.v_cache)
+    qs = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    q = torch.randn((int(qs[-1]), H, D), generator=gen, device="cuda").to(tdt)
+    print(f"[prefill] long prompts {dt} D={D} bs={bs}: {int(qs[-1])} queries", flush=True)
+    args = (q, w.k_cache, w.v_cache, w.block_tables, torch.from_numpy(qs).cuda(), w.context_lens, cfg.scale,
+            int(news.max()))
+    out = pkv.paged_attention_prefill(*args)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    kc, vc, qh = W.storage_numpy(w.k_cache), W.storage_numpy(w.v_cache), W.storage_numpy(q)
+    rows, ctx, tabs = [], [], []
+    for i in range(3):
+        first = int(lens[i] - news[i])
+        pick = sorted({0, int(news[i]) - 1} | set(rng.choice(int(news[i]), size=30, replace=False).tolist()))
+        for j in pick:
+            rows.append(int(qs[i]) + j)
+            ctx.append(first + j + 1)
+            tabs.append(meta.block_tables[i])
+    ref = oracle.decode(qh[rows], kc, vc, np.stack(tabs), np.array(ctx), cfg.scale, bs, dt)
+    err, rel = check(got[rows], ref, dt, f"long prompts {dt} D{D} bs{bs}")
+    print(f"  {len(rows)} rows: max-abs {err:.2e} rel-L2 {rel:.2e}", flush=True)
+    for _ in range(3):
+        again = pkv.paged_attention_prefill(*args)
+        assert torch.equal(again.view(torch.int16), out.view(torch.int16))
+
+
 def test_prefill_contract(pkv, monkeypatch):
     rng = np.random.default_rng(520)
     c = P.Case(rng, [600, 20], H=2, D=64, bs=16, dtype="f32")
