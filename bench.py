@@ -105,6 +105,38 @@ def cpu_baseline(meta, w, budget_s=10.0):
             "tokens_heads_per_s": round(tokens / wall, 1)}
 
 
+def cpu_baseline_prefill(q, kc, vc, tables, lens, scale, bs, dtype, budget_s=10.0):
+    """The oracle's prefill, untouched, on the same prompts: one prompt after another (its queries over its own
+    cache blocks) until about budget_s; only finished prompts count."""
+    import numpy as np
+    import resource
+
+    import oracle
+    import workloads as W
+    qh, kh, vh = W.storage_numpy(q), W.storage_numpy(kc), W.storage_numpy(vc)
+    H, D = qh.shape[1], qh.shape[2]
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    tokens, pairs, done = 0, 0, 0
+    cpu0 = resource.getrusage(resource.RUSAGE_SELF)
+    t0 = time.perf_counter()
+    for i, P in enumerate(lens.tolist()):
+        if time.perf_counter() - t0 >= budget_s:
+            break
+        oracle.prefill(qh[starts[i]:starts[i] + P], kh, vh, tables[i:i + 1], np.array([0, P]), np.array([P]),
+                       scale, bs, dtype)
+        tokens += P
+        pairs += P * (P + 1) // 2
+        done += 1
+    wall = time.perf_counter() - t0
+    cpu1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (cpu1.ru_utime - cpu0.ru_utime) + (cpu1.ru_stime - cpu0.ru_stime)
+    return {"value": round(tokens / wall, 1), "unit": "prompt tokens/s", "cores": max(1, round(cpu / wall)),
+            "kind": "oracle",
+            "sample": f"{done} of the {len(lens)} prompts ({tokens} tokens), each prefilled alone; "
+                      f"{wall:.1f} s wall, {cpu:.1f} s CPU",
+            "tflops": round(pairs * H * 4 * D / wall / 1e12, 6)}
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partition_llama13b_b64_hbm_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_383_amd", "csrc", f) for f in ("decode.hip", "pkv_internal.h")]
 
@@ -482,6 +514,14 @@ def prefill(args):
                      "algorithmic_flops_per_launch": flops, "mean_launch_us": round(pre_us, 2)},
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle's prefill on a sample of the same prompts ...")
+        order_short = np.argsort(lens, kind="stable")           # shortest prompts first: more of them fit
+        sub = [int(x) for x in order_short]
+        qs_sub = np.concatenate([[0], np.cumsum(lens[sub])])
+        q_sub = torch.cat([q[int(qs[i]):int(qs[i + 1])] for i in sub])
+        rec["cpu_baseline"] = cpu_baseline_prefill(q_sub, kc, vc, tables[sub], lens[sub], cfg.scale, bs, cfg.dtype)
+        log(f"cpu oracle: {rec['cpu_baseline']}")
     print(json.dumps(rec), flush=True)
 
 
