@@ -183,7 +183,10 @@ int paged_attention_decode(const void* q, const void* k_cache, const void* v_cac
  * rounded to nearest even.  Caller contract, checked under PKV_DEBUG=1:
  * P_i <= max_query_len, P_i <= L_i <= max_blocks_per_seq * block_size, block ids
  * in range; a sequence that breaks it gets NaN rows, and no memory outside the
- * arrays is touched.  Returns PKV_OK, or an error status with nothing launched.
+ * arrays is touched.  Returns PKV_OK, or an error status with nothing launched:
+ * PKV_EUNSUPPORTED when num_heads, num_seqs or ceil(max_query_len / 128)
+ * exceeds 65535, or (16-bit types) when the launch of one 256-thread
+ * work-group per (sequence, head, 128-query tile) would exceed 2^32 threads.
  */
 int paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                             int32_t max_blocks_per_seq, const int32_t* query_start, const int32_t* context_lens,
