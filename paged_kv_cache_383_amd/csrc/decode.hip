@@ -229,32 +229,33 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
   const int j0 = p * part_blocks;
   const int j1 = min(j0 + part_blocks, nb);
 
-  // Decode step with the append fused in (k_new given): the work-group whose
-  // partition holds the newest token, position L - 1, first stores that
-  // token's K and V rows of its head into their slot ("vLLM KV cache and
-  // PagedAttention explained", Step 6: the decode token's K/V goes to the next
-  // slot of the sequence's last block), waits for the stores, and only then
-  // lets its waves read the block.
-  if (k_new != nullptr && p == parts - 1) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // Decode step with the append fused in (k_new given): in the work-group
+  // whose partition holds the newest token, position L - 1, the one wave that
+  // reads that token's block first stores the token's K and V rows of its head
+  // into their slot ("vLLM KV cache and PagedAttention explained", Step 6: the
+  // decode token's K/V goes to the next slot of the sequence's last block) and
+  // waits for its stores before it issues any load; the other waves never read
+  // that block and start at once.
+  if (k_new != nullptr && p == parts - 1 && wave == ((nb - 1 - j0) / TPS) % kWaves) {
     const int32_t bl = block_tables[int64_t(s) * max_blocks + (L - 1) / BS];
     if (static_cast<uint64_t>(static_cast<int64_t>(bl)) < static_cast<uint64_t>(num_blocks)) {
       constexpr int kVecRow = G::kRowBytes / 16;
+      static_assert(2 * kVecRow <= 64, "one wave stores the K and V rows");
       const int64_t dst = ((int64_t(bl) * gridDim.x + blockIdx.x) * BS + (L - 1) % BS) * G::kRowBytes;
       const int64_t src = row * G::kRowBytes;
-      const int i = threadIdx.x;
-      if (i < kVecRow) {
-        *reinterpret_cast<u32x4*>(k_cache + dst + 16 * i) = *reinterpret_cast<const u32x4*>(k_new + src + 16 * i);
-      } else if (i < 2 * kVecRow) {
-        const int c = i - kVecRow;
-        *reinterpret_cast<u32x4*>(v_cache + dst + 16 * c) = *reinterpret_cast<const u32x4*>(v_new + src + 16 * c);
+      if (lane < kVecRow) {
+        *reinterpret_cast<u32x4*>(k_cache + dst + 16 * lane) = *reinterpret_cast<const u32x4*>(k_new + src + 16 * lane);
+      } else if (lane < 2 * kVecRow) {
+        const int cv = lane - kVecRow;
+        *reinterpret_cast<u32x4*>(v_cache + dst + 16 * cv) = *reinterpret_cast<const u32x4*>(v_new + src + 16 * cv);
       }
       __builtin_amdgcn_s_waitcnt(0);                 // the stores have reached the L2 the loads read
     }
-    __syncthreads();
   }
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane / G::kLpr;                           // token row within a wave-wide load
   const int c = lane % G::kLpr;                           // 16-byte column within the row
 
