@@ -34,7 +34,10 @@
  * between calls and never retains a pointer.  `stream` is a hipStream_t passed
  * as void* (NULL = the legacy default stream).  All work is enqueued
  * asynchronously on `stream`; nothing synchronises with the host except in
- * PKV_DEBUG mode (below).  Outputs must not alias inputs.
+ * PKV_DEBUG mode (below).  Outputs must not alias inputs.  Arrays of
+ * elements (q, k, v, k_new, v_new, the caches, out) and the workspace are
+ * moved in 16-byte vectors and must be 16-byte aligned; int32 metadata must be
+ * 4-byte and int64 metadata 8-byte aligned (PKV_EINVAL otherwise).
  *
  * Errors.  Every call validates its scalar arguments and pointers on the host
  * before any HIP call; on failure it returns a non-zero pkv_status, launches

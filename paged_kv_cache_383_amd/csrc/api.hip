@@ -65,6 +65,9 @@ int check_shape(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t bloc
   return PKV_OK;
 }
 
+// Element arrays move in 16-byte vectors; metadata is read in whole words.
+bool misaligned(const void* p, uintptr_t n) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & (n - 1)) != 0; }
+
 int hip_fail(hipError_t e, const char* what) {
   return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -129,6 +132,9 @@ extern "C" int paged_kv_write(const void* k, const void* v, const int64_t* slot_
   if (num_tokens == 0) return ok();
   if (!k || !v || !slot_mapping || !k_cache || !v_cache)
     return fail(PKV_EINVAL, "null pointer among k, v, slot_mapping, k_cache, v_cache");
+  if (misaligned(k, 16) || misaligned(v, 16) || misaligned(k_cache, 16) || misaligned(v_cache, 16) ||
+      misaligned(slot_mapping, 8))
+    return fail(PKV_EINVAL, "k, v, k_cache and v_cache must be 16-byte aligned, slot_mapping 8-byte aligned");
   const int64_t vecs = num_tokens * int64_t(num_heads) * (head_dim * elem_bytes(dtype) / 16);
   if (vecs / 256 >= (int64_t(1) << 31) - 1) return fail(PKV_EUNSUPPORTED, "num_tokens %lld too large for one launch", (long long)num_tokens);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -162,6 +168,8 @@ extern "C" int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int64_t*
   if (num_pairs == 0) return ok();
   if (!k_cache || !v_cache || !block_mapping)
     return fail(PKV_EINVAL, "null pointer among k_cache, v_cache, block_mapping");
+  if (misaligned(k_cache, 16) || misaligned(v_cache, 16) || misaligned(block_mapping, 8))
+    return fail(PKV_EINVAL, "k_cache and v_cache must be 16-byte aligned, block_mapping 8-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (debug_checks()) {
     std::vector<int64_t> m(size_t(2 * num_pairs));
@@ -198,6 +206,10 @@ extern "C" int paged_kv_prepare_step(int32_t* block_tables, int32_t max_blocks_p
   if (num_seqs == 0 && num_updates == 0) return ok();
   if (!block_tables || !context_lens || (num_updates > 0 && !updates))
     return fail(PKV_EINVAL, "null pointer among block_tables, context_lens, updates");
+  if (misaligned(block_tables, 4) || misaligned(context_lens, 4) || misaligned(updates, 4) ||
+      misaligned(new_lens, 4) || misaligned(slot_mapping, 8))
+    return fail(PKV_EINVAL, "block_tables, context_lens, updates and new_lens must be 4-byte aligned, "
+                "slot_mapping 8-byte aligned");
   hipError_t e = pkv::launch_prepare_step(block_tables, max_blocks_per_seq, context_lens, num_seqs, updates,
                                           num_updates, new_lens, slot_mapping, block_size, num_blocks,
                                           static_cast<hipStream_t>(stream));
@@ -222,6 +234,10 @@ extern "C" int paged_attention_prefill(const void* q, const void* k_cache, const
   if (num_seqs == 0 || max_query_len == 0) return ok();
   if (!q || !k_cache || !v_cache || !block_tables || !query_start || !context_lens || !out)
     return fail(PKV_EINVAL, "null pointer among q, k_cache, v_cache, block_tables, query_start, context_lens, out");
+  if (misaligned(q, 16) || misaligned(k_cache, 16) || misaligned(v_cache, 16) || misaligned(out, 16) ||
+      misaligned(block_tables, 4) || misaligned(query_start, 4) || misaligned(context_lens, 4))
+    return fail(PKV_EINVAL, "q, k_cache, v_cache and out must be 16-byte aligned, block_tables, query_start and "
+                "context_lens 4-byte aligned");
   const int64_t tq = pkv::prefill_tile_queries(dtype);
   const int64_t tiles = (int64_t(max_query_len) + tq - 1) / tq;
   if (num_heads > 65535 || num_seqs > 65535 || tiles > 65535)
@@ -300,6 +316,11 @@ int decode_common(const void* q, const void* k_new, const void* v_new, const voi
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return fail(PKV_EINVAL, "null pointer among q, k_cache, v_cache, block_tables, context_lens, out");
   if ((k_new == nullptr) != (v_new == nullptr)) return fail(PKV_EINVAL, "k_new and v_new must both be given");
+  if (misaligned(q, 16) || misaligned(k_cache, 16) || misaligned(v_cache, 16) || misaligned(out, 16) ||
+      misaligned(k_new, 16) || misaligned(v_new, 16) || misaligned(workspace, 16) || misaligned(block_tables, 4) ||
+      misaligned(context_lens, 4))
+    return fail(PKV_EINVAL, "q, k_new, v_new, k_cache, v_cache, out and workspace must be 16-byte aligned, "
+                "block_tables and context_lens 4-byte aligned");
   if (num_heads > 65535 || num_seqs > 65535)
     return fail(PKV_EUNSUPPORTED, "num_heads %d / num_seqs %d exceed the grid limit 65535", num_heads, num_seqs);
   const int32_t pb = part_blocks_for(max_blocks_per_seq, block_size, partition_size);

@@ -404,9 +404,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const float inv = any_bad ? __builtin_nanf("") : 1.f / lt;
     const int64_t base = (int64_t(qa + qi) * H + h) * D;
 #pragma unroll
-    for (int t = 0; t < kDTiles; ++t)
+    for (int t = 0; t < kDTiles; ++t) {
+      if constexpr (DT == PKV_F32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + base + 16 * t + 4 * grp) = acc[u][t] * inv;
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) store_out<DT>(out, base + 16 * t + 4 * grp + e, acc[u][t][e] * inv);
+        for (int e = 0; e < 4; ++e) store_out<DT>(out, base + 16 * t + 4 * grp + e, acc[u][t][e] * inv);
+      }
+    }
   }
 }
 
@@ -467,6 +472,19 @@ __device__ inline void load_lds16(const char* base, int nrec, uint32_t voff, uin
 }
 __device__ inline uint32_t lds_address(const void* p) {
   return static_cast<uint32_t>((uintptr_t)(__attribute__((address_space(3))) const void*)p);
+}
+
+// Two fp32 values rounded to nearest even into one word of 16-bit elements
+// (the first in the low half).
+template <int DT>
+__device__ inline uint32_t pack2(float x, float y) {
+  if constexpr (DT == PKV_BF16) {
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, v2{static_cast<__bf16>(x), static_cast<__bf16>(y)});
+  } else {
+    typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, v2{static_cast<_Float16>(x), static_cast<_Float16>(y)});
+  }
 }
 
 template <int DT, int D, int BS>
@@ -736,11 +754,24 @@ __global__ __launch_bounds__(64 * kWaves32) __attribute__((amdgpu_waves_per_eu(3
   const float lt = hl.lo + hl.hi;
   if (qi >= P) return;
   const float inv = sm_bad ? __builtin_nanf("") : 1.f / lt;
-  const int64_t base = (int64_t(qa + qi) * H + h) * D;
+  // Lane (query, half hh) holds dims 32 t + 8 g + 4 hh + (0..3) of its
+  // query.  Packed into 16-bit pairs and exchanged across the lane halves
+  // (group g = 2 m with g = 2 m + 1), each lane ends with the 8 consecutive
+  // dims 32 t + 16 m + 8 hh + (0..7) and writes them with one 16-byte store.
+  E* orow = static_cast<E*>(out) + (int64_t(qa + qi) * H + h) * D;
 #pragma unroll
   for (int t = 0; t < kDTiles; ++t)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) store_out<DT>(out, base + 32 * t + 8 * (e / 4) + 4 * hh + e % 4, acc[t][e] * inv);
+    for (int m = 0; m < 2; ++m) {
+      const f32x16& a = acc[t];
+      const uint32_t a0 = pack2<DT>(a[8 * m] * inv, a[8 * m + 1] * inv);
+      const uint32_t a1 = pack2<DT>(a[8 * m + 2] * inv, a[8 * m + 3] * inv);
+      const uint32_t b0 = pack2<DT>(a[8 * m + 4] * inv, a[8 * m + 5] * inv);
+      const uint32_t b1 = pack2<DT>(a[8 * m + 6] * inv, a[8 * m + 7] * inv);
+      const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+      *reinterpret_cast<u32x4*>(orow + 32 * t + 16 * m + 8 * hh) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+    }
 }
 
 template <int DT, int D, int BS>

@@ -106,6 +106,10 @@ cases = [
   ("pf_zero_seqs", lambda: pf(B=0, q=None), 0), ("pf_zero_q", lambda: pf(mq=0, q=None), 0),
   ("pf_neg_q", lambda: pf(mq=-5), 1), ("pf_null_qs", lambda: pf(qs=None), 1),
   ("pf_scale", lambda: pf(scale=float("nan")), 1), ("pf_grid", lambda: pf(mq=1 << 30), 2),
+  ("dec_misaligned_q", lambda: dec(q=F + 8), 1), ("dec_misaligned_tab", lambda: dec(tab=F + 2), 1),
+  ("dec_misaligned_ws", lambda: dec(ws=F + 4), 1), ("wr_misaligned_cache", lambda: wr(kc=F + 4), 1),
+  ("wr_misaligned_slots", lambda: wr(s=F + 4), 1), ("cp_misaligned_pairs", lambda: cp(m=F + 4), 1),
+  ("pf_misaligned_out", lambda: pf(out=F + 2), 1), ("pf_misaligned_qs", lambda: pf(qs=F + 1), 1),
 ]
 for name, call, want in cases:
     got = call()
@@ -154,6 +158,8 @@ def test_error_messages_name_the_problem(libpath):
     assert "workspace" in msgs["dec_ws_small"]
     assert "partition_size 100" in msgs["dec_part"]
     assert msgs["dec_zero_seqs"] == "''"
+    assert "16-byte aligned" in msgs["dec_misaligned_q"] and "16-byte aligned" in msgs["pf_misaligned_out"]
+    assert "8-byte aligned" in msgs["wr_misaligned_slots"]
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
