@@ -641,6 +641,10 @@ __global__ __launch_bounds__(64 * kWaves32) __attribute__((amdgpu_waves_per_eu(3
 
   auto compute = [&](int c, const E* sk, const E* sv) {
     const int k0 = c * kChunk;
+    // Matrix products issue at raised wave priority, so that a wave with
+    // products ready goes ahead of the other waves' softmax arithmetic on its
+    // SIMD (measured 1-3 % faster).
+    __builtin_amdgcn_s_setprio(1);
     // S^T (32 keys x 32 queries).
     f32x16 st;
 #pragma unroll
@@ -653,6 +657,7 @@ __global__ __launch_bounds__(64 * kWaves32) __attribute__((amdgpu_waves_per_eu(3
       else
         st = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[k], st, 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
     // Mask, running max (in-lane over 16 keys, then across the lane halves).
     // The scale (> 0) keeps the order of scores, so the max is taken on the
     // raw products and the scale enters once per key, in the exponent's fma.
@@ -690,6 +695,7 @@ __global__ __launch_bounds__(64 * kWaves32) __attribute__((amdgpu_waves_per_eu(3
 #pragma unroll
       for (int t = 0; t < kDTiles; ++t) acc[t] *= alpha;
     }
+    __builtin_amdgcn_s_setprio(1);
     // O^T += V^T P^T: per 32-dim tile, two k-steps of 16 keys.
 #pragma unroll
     for (int t = 0; t < kDTiles; ++t)
@@ -705,6 +711,7 @@ __global__ __launch_bounds__(64 * kWaves32) __attribute__((amdgpu_waves_per_eu(3
         else
           acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[ks], acc[t], 0, 0, 0);
       }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Chunk c: wait for this wave's loads of chunk c (those of chunk c + 1 may
