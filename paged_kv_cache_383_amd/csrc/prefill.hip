@@ -691,7 +691,7 @@ __global__ __launch_bounds__(64 * kWaves32) __attribute__((amdgpu_waves_per_eu(3
       pf[e / 8][e % 8] = Mfma<DT>::from_f32(pe);
     }
     l = l * alpha + ps;
-    if (__any(alpha != 1.f)) {
+    if (c > 0 && __any(alpha != 1.f)) {           // chunk 0: acc is still zero
 #pragma unroll
       for (int t = 0; t < kDTiles; ++t) acc[t] *= alpha;
     }
