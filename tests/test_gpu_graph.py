@@ -1,0 +1,130 @@
+"""Graph capture: the library's GPU calls can be recorded into a HIP graph (torch.cuda.CUDAGraph on ROCm)
+and replayed.
+
+Every call launches on the stream it is given (the binding passes torch's current stream) and allocates,
+copies, clears and synchronises nothing, so a captured call is its kernels alone.  Each test captures a call
+once and replays the graph several times, with the program's own eager work and synchronisations between the
+replays, and checks every replay bit for bit against the same call made eagerly.
+"""
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_kv_cache_383_amd import build as b
+    if not os.path.exists(b.LIB_PATH):
+        b.build()
+    import paged_kv_cache_383_amd as m
+    m.lib()
+    return m
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def same_bits(a, b):
+    it = {2: torch.int16, 4: torch.int32}[a.element_size()]
+    return torch.equal(a.view(it), b.view(it))
+
+
+def capture(fn):
+    """Warm fn up on a side stream, then record it into a graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("part", [0, 512])
+def test_decode_step_graph_replays_match_eager(pkv, part):
+    lens = np.random.default_rng(11).integers(100, 1500, 12)
+    meta = W.make_metadata(2, lens=lens)
+    cfg = meta.cfg
+    say(f"graph decode step: B={len(lens)} H={cfg.num_heads} D={cfg.head_dim} partition={part}")
+    wl = W.make_workload(meta, "cuda")
+    B, H, D, bs, M = len(lens), cfg.num_heads, cfg.head_dim, cfg.block_size, cfg.max_blocks
+    ws = torch.zeros(max(pkv.paged_attention_workspace_bytes(B, H, D, M, bs, part), 1), dtype=torch.uint8,
+                     device="cuda")
+
+    kc_e, vc_e = wl.k_cache.clone(), wl.v_cache.clone()
+    out_e = pkv.paged_attention_decode_step(wl.q, wl.k_new, wl.v_new, kc_e, vc_e, wl.block_tables,
+                                            wl.context_lens, cfg.scale, workspace=ws, partition_size=part)
+    torch.cuda.synchronize()
+
+    kc, vc = wl.k_cache.clone(), wl.v_cache.clone()
+    out = torch.empty_like(wl.q)
+    g = capture(lambda: pkv.paged_attention_decode_step(wl.q, wl.k_new, wl.v_new, kc, vc, wl.block_tables,
+                                                        wl.context_lens, cfg.scale, out=out, workspace=ws,
+                                                        partition_size=part))
+    for r in range(3):
+        out.fill_(float("nan"))
+        kc.copy_(wl.k_cache)
+        vc.copy_(wl.v_cache)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {r}")
+        assert same_bits(out, out_e), f"replay {r}: output differs from the eager call"
+        assert same_bits(kc, kc_e) and same_bits(vc, vc_e), f"replay {r}: cache differs from the eager call"
+
+
+def test_prefill_graph_replays_match_eager(pkv):
+    rng = np.random.default_rng(12)
+    H, D, bs, dt = 8, 128, 16, torch.bfloat16
+    prompts = np.array([200, 77, 513])
+    say(f"graph prefill: prompts={prompts.tolist()} H={H} D={D} bs={bs}")
+    nblk = (prompts + bs - 1) // bs
+    NB = int(nblk.sum()) + 5
+    ids = rng.permutation(NB).astype(np.int32)
+    width = int(nblk.max())
+    tables = np.full((len(prompts), width), -1, np.int32)
+    pos = 0
+    for i, n in enumerate(nblk):
+        tables[i, :n] = ids[pos:pos + n]
+        pos += n
+    T = int(prompts.sum())
+    slots = np.concatenate([[tables[i][t // bs] * bs + t % bs for t in range(P)] for i, P in enumerate(prompts)])
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(12)
+    q = torch.randn((T, H, D), generator=gen, device="cuda").to(dt)
+    k = torch.randn((T, H, D), generator=gen, device="cuda").to(dt)
+    v = torch.randn((T, H, D), generator=gen, device="cuda").to(dt)
+    kc = torch.zeros((NB, H, bs, D), dtype=dt, device="cuda")
+    vc = torch.zeros_like(kc)
+    pkv.paged_kv_write(k, v, torch.from_numpy(slots.astype(np.int64)).cuda(), kc, vc)
+    t_tab = torch.from_numpy(tables).cuda()
+    t_qs = torch.from_numpy(np.concatenate([[0], np.cumsum(prompts)]).astype(np.int32)).cuda()
+    t_len = torch.from_numpy(prompts.astype(np.int32)).cuda()
+    scale = 1.0 / np.sqrt(D)
+    maxq = int(prompts.max())
+    out_e = pkv.paged_attention_prefill(q, kc, vc, t_tab, t_qs, t_len, scale, maxq)
+    torch.cuda.synchronize()
+
+    out = torch.empty_like(q)
+    g = capture(lambda: pkv.paged_attention_prefill(q, kc, vc, t_tab, t_qs, t_len, scale, maxq, out=out))
+    for r in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {r}")
+        assert same_bits(out, out_e), f"replay {r}: output differs from the eager call"
