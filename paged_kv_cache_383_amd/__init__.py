@@ -109,12 +109,18 @@ def _check(status: int):
         raise PagedKVError(status, last_error())
 
 
+_DTYPE_CODES = None
+
+
 def _dtype_code(t) -> int:
-    import torch
-    codes = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
-    if t.dtype not in codes:
+    global _DTYPE_CODES
+    if _DTYPE_CODES is None:
+        import torch
+        _DTYPE_CODES = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+    code = _DTYPE_CODES.get(t.dtype)
+    if code is None:
         raise TypeError(f"unsupported dtype {t.dtype}")
-    return codes[t.dtype]
+    return code
 
 
 def _device_tensor(name, t, dtype=None, ndim=None):
@@ -128,9 +134,31 @@ def _device_tensor(name, t, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
 
 
-def _stream(device):
+def _stream(index: int) -> int:
+    """torch's current stream on device ``index``, as the raw hipStream_t."""
     import torch
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    return raw(index) if raw is not None else torch.cuda.current_stream(index).cuda_stream
+
+
+def _launch(device, fn, *args):
+    """fn(*args, stream) on torch's current stream of ``device``, with that device current during the call
+    (switched only when another one is)."""
+    import torch
+    if torch.cuda.current_device() == device.index:
+        return fn(*args, _stream(device.index))
+    with torch.cuda.device(device):
+        return fn(*args, _stream(device.index))
+
+
+def _workspace(workspace, device, B, H, D, M, bs, partition_size):
+    """The caller's workspace (checked; the library checks its size), or a new one of the size needed."""
+    import torch
+    if workspace is not None:
+        _device_tensor("workspace", workspace)
+        return workspace
+    need = paged_attention_workspace_bytes(B, H, D, M, bs, partition_size)
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
 
 
 def paged_kv_write(k, v, slot_mapping, k_cache, v_cache):
@@ -144,10 +172,8 @@ def paged_kv_write(k, v, slot_mapping, k_cache, v_cache):
     NB, H, bs, D = k_cache.shape
     if k.shape[1:] != (H, D) or slot_mapping.shape[0] != k.shape[0]:
         raise ValueError("k/v/slot_mapping shapes do not match the cache")
-    with torch.cuda.device(k_cache.device):
-        _check(lib().paged_kv_write(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k.shape[0],
-                                    k_cache.data_ptr(), v_cache.data_ptr(), NB, H, D, bs,
-                                    _dtype_code(k_cache), _stream(k_cache.device)))
+    _check(_launch(k_cache.device, lib().paged_kv_write, k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
+                   k.shape[0], k_cache.data_ptr(), v_cache.data_ptr(), NB, H, D, bs, _dtype_code(k_cache)))
 
 
 def paged_attention_partition_size(num_seqs, num_heads, max_blocks_per_seq, block_size,
@@ -185,18 +211,11 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
     M = block_tables.shape[1]
-    need = paged_attention_workspace_bytes(B, H, D, M, bs, partition_size)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    else:
-        _device_tensor("workspace", workspace)
+    workspace = _workspace(workspace, q.device, B, H, D, M, bs, partition_size)
     ws_bytes = workspace.numel() * workspace.element_size()
-    with torch.cuda.device(q.device):
-        _check(lib().paged_attention_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                            block_tables.data_ptr(), M, context_lens.data_ptr(), B, H, D,
-                                            bs, NB, float(scale), _dtype_code(q), out.data_ptr(),
-                                            workspace.data_ptr(), ws_bytes, partition_size,
-                                            _stream(q.device)))
+    _check(_launch(q.device, lib().paged_attention_decode, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                   block_tables.data_ptr(), M, context_lens.data_ptr(), B, H, D, bs, NB, float(scale),
+                   _dtype_code(q), out.data_ptr(), workspace.data_ptr(), ws_bytes, partition_size))
     return out
 
 
@@ -225,18 +244,12 @@ def paged_attention_decode_step(q, k_new, v_new, k_cache, v_cache, block_tables,
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
     M = block_tables.shape[1]
-    need = paged_attention_workspace_bytes(B, H, D, M, bs, partition_size)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    else:
-        _device_tensor("workspace", workspace)
+    workspace = _workspace(workspace, q.device, B, H, D, M, bs, partition_size)
     ws_bytes = workspace.numel() * workspace.element_size()
-    with torch.cuda.device(q.device):
-        _check(lib().paged_attention_decode_step(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
-                                                 k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), M,
-                                                 context_lens.data_ptr(), B, H, D, bs, NB, float(scale),
-                                                 _dtype_code(q), out.data_ptr(), workspace.data_ptr(), ws_bytes,
-                                                 partition_size, _stream(q.device)))
+    _check(_launch(q.device, lib().paged_attention_decode_step, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                   k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), M, context_lens.data_ptr(), B,
+                   H, D, bs, NB, float(scale), _dtype_code(q), out.data_ptr(), workspace.data_ptr(), ws_bytes,
+                   partition_size))
     return out
 
 
@@ -263,11 +276,9 @@ def paged_attention_prefill(q, k_cache, v_cache, block_tables, query_start, cont
         _device_tensor("out", out, q.dtype, 3)
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
-    with torch.cuda.device(q.device):
-        _check(lib().paged_attention_prefill(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                             block_tables.data_ptr(), block_tables.shape[1], query_start.data_ptr(),
-                                             context_lens.data_ptr(), B, int(max_query_len), H, D, bs, NB,
-                                             float(scale), _dtype_code(q), out.data_ptr(), _stream(q.device)))
+    _check(_launch(q.device, lib().paged_attention_prefill, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                   block_tables.data_ptr(), block_tables.shape[1], query_start.data_ptr(), context_lens.data_ptr(),
+                   B, int(max_query_len), H, D, bs, NB, float(scale), _dtype_code(q), out.data_ptr()))
     return out
 
 
@@ -280,10 +291,8 @@ def paged_kv_copy_blocks(k_cache, v_cache, block_mapping):
     if v_cache.shape != k_cache.shape or block_mapping.shape[1] != 2:
         raise ValueError("caches must match and block_mapping must be [N, 2]")
     NB, H, bs, D = k_cache.shape
-    with torch.cuda.device(k_cache.device):
-        _check(lib().paged_kv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), block_mapping.data_ptr(),
-                                          block_mapping.shape[0], NB, H, D, bs, _dtype_code(k_cache),
-                                          _stream(k_cache.device)))
+    _check(_launch(k_cache.device, lib().paged_kv_copy_blocks, k_cache.data_ptr(), v_cache.data_ptr(),
+                   block_mapping.data_ptr(), block_mapping.shape[0], NB, H, D, bs, _dtype_code(k_cache)))
 
 
 class BlockPool:
@@ -393,12 +402,10 @@ def paged_kv_prepare_step(block_tables, context_lens, updates, new_lens, slot_ma
         _device_tensor("new_lens", new_lens, torch.int32, 1)
     if slot_mapping is not None:
         _device_tensor("slot_mapping", slot_mapping, torch.int64, 1)
-    with torch.cuda.device(block_tables.device):
-        _check(lib().paged_kv_prepare_step(block_tables.data_ptr(), width, context_lens.data_ptr(), rows,
-                                           None if updates is None else updates.data_ptr(), n,
-                                           None if new_lens is None else new_lens.data_ptr(),
-                                           None if slot_mapping is None else slot_mapping.data_ptr(),
-                                           int(block_size), int(num_blocks), _stream(block_tables.device)))
+    _check(_launch(block_tables.device, lib().paged_kv_prepare_step, block_tables.data_ptr(), width,
+                   context_lens.data_ptr(), rows, None if updates is None else updates.data_ptr(), n,
+                   None if new_lens is None else new_lens.data_ptr(),
+                   None if slot_mapping is None else slot_mapping.data_ptr(), int(block_size), int(num_blocks)))
 
 
 class Batch:

@@ -128,3 +128,13 @@ def test_prefill_graph_replays_match_eager(pkv):
         torch.cuda.synchronize()
         say(f"  replay {r}")
         assert same_bits(out, out_e), f"replay {r}: output differs from the eager call"
+
+
+def test_binding_launches_on_torch_current_stream(pkv):
+    """The stream handed to the library is torch's current stream, also inside a stream context."""
+    dev = torch.cuda.current_device()
+    assert pkv._stream(dev) == torch.cuda.current_stream(dev).cuda_stream
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert pkv._stream(dev) == side.cuda_stream
+    assert pkv._stream(dev) == torch.cuda.current_stream(dev).cuda_stream
