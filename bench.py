@@ -657,9 +657,32 @@ def main():
     ev3.record()
     torch.cuda.synchronize()
     write_us = ev2.elapsed_time(ev3) * 1e3 / args.steps
+    # Timed region 4: the fused steps recorded once into a HIP graph (one step per input set, in rotation
+    # order) and replayed: the step without the host's per-call work, which bounds the small configurations.
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fused_step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(rotate):
+            fused_step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // rotate)
+    ev2.record()
+    for _ in range(reps):
+        g.replay()
+    ev3.record()
+    torch.cuda.synchronize()
+    graph_us = ev2.elapsed_time(ev3) * 1e3 / (reps * rotate)
+    del g
     achieved = nbytes["decode"] / (decode_us * 1e-6) / 1e9
     log(f"step {step_s * 1e6:.1f} us (wall; {step_ev_us:.1f} us by events; "
-        f"{'fused' if args.two_call_step else 'two-call'} step {other_us:.1f} us), decode {decode_us:.1f} us, "
+        f"{'fused' if args.two_call_step else 'two-call'} step {other_us:.1f} us; fused step from a HIP graph "
+        f"{graph_us:.1f} us), decode {decode_us:.1f} us, "
         f"write {write_us:.1f} us -> decode {achieved:.0f} GB/s = {achieved / PEAK_HBM_GBS:.1%} of peak")
 
     cpu = None
@@ -702,9 +725,11 @@ def main():
         "fraction_of_peak": round(nbytes["step"] / step_s / 1e9 / PEAK_HBM_GBS, 4),
         "kernels_us": {"paged_kv_write": round(write_us, 2), "paged_attention_decode": round(decode_us, 2),
                        "step_by_events": round(step_ev_us, 2),
-                       ("paged_attention_decode_step" if args.two_call_step else "two_call_step"): round(other_us, 2)},
+                       ("paged_attention_decode_step" if args.two_call_step else "two_call_step"): round(other_us, 2),
+                       "fused_step_graph_replay": round(graph_us, 2)},
         "roofline": {
-            "kernel": "paged_attention_decode (decode_partition_kernel" + (" + lse_reduce_kernel)" if resolved else ")"),
+            "kernel": ("paged_attention_decode (decode_partition_kernel"
+                       + (" + lse_reduce_kernel)" if resolved else ")")),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
