@@ -203,7 +203,7 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ bool context_ok(int32_t L, int32_t cap) { return L >= 0 && L <= cap; }
 
-template <int DT, int D, int BS, int WAVES, int TPS, int NST>
+template <int DT, int D, int BS, int WAVES, int TPS, int NST, bool FUSED>
 __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
     const void* __restrict__ q, char* __restrict__ k_cache, char* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
@@ -232,32 +232,39 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // Decode step with the append fused in (k_new given): in the work-group
-  // whose partition holds the newest token, position L - 1, the one wave that
-  // reads that token's block first stores the token's K and V rows of its head
-  // into their slot ("vLLM KV cache and PagedAttention explained", Step 6: the
-  // decode token's K/V goes to the next slot of the sequence's last block) and
-  // waits for its stores before it issues any load; the other waves never read
-  // that block and start at once.
-  if (k_new != nullptr && p == parts - 1 && wave == ((nb - 1 - j0) / TPS) % kWaves) {
-    const int32_t bl = block_tables[int64_t(s) * max_blocks + (L - 1) / BS];
-    if (static_cast<uint64_t>(static_cast<int64_t>(bl)) < static_cast<uint64_t>(num_blocks)) {
-      constexpr int kVecRow = G::kRowBytes / 16;
-      static_assert(2 * kVecRow <= 64, "one wave stores the K and V rows");
-      const int64_t dst = ((int64_t(bl) * gridDim.x + blockIdx.x) * BS + (L - 1) % BS) * G::kRowBytes;
-      const int64_t src = row * G::kRowBytes;
-      if (lane < kVecRow) {
-        *reinterpret_cast<u32x4*>(k_cache + dst + 16 * lane) = *reinterpret_cast<const u32x4*>(k_new + src + 16 * lane);
-      } else if (lane < 2 * kVecRow) {
-        const int cv = lane - kVecRow;
-        *reinterpret_cast<u32x4*>(v_cache + dst + 16 * cv) = *reinterpret_cast<const u32x4*>(v_new + src + 16 * cv);
-      }
-      __builtin_amdgcn_s_waitcnt(0);                 // the stores have reached the L2 the loads read
-    }
-  }
-
   const int r = lane / G::kLpr;                           // token row within a wave-wide load
   const int c = lane % G::kLpr;                           // 16-byte column within the row
+
+  // Decode step with the append fused in (k_new given).  The newest token,
+  // position L - 1, goes to its slot of the sequence's last block ("vLLM KV
+  // cache and PagedAttention explained", Step 6: the decode token's K/V goes
+  // to the next slot of the sequence's last block).  Only one wave of one
+  // work-group per (sequence, head) reads that block: the wave of the last
+  // partition whose stages hold block nb - 1.  That wave takes the new row's
+  // 16-byte column c straight from k_new / v_new into registers here, puts it
+  // in place of the cache row when it consumes the stage, and stores it to
+  // the cache without waiting for the store: no load of this launch depends
+  // on it.  The values used are the same bits a write-then-read would return.
+  int i_new = -1;                                         // stage index holding the newest row (owner wave)
+  int x_new = 0;                                          // its row slot within the stage buffers
+  bool lane_new = false;                                  // this lane holds a column of the newest row
+  int64_t dst_new = -1;                                   // byte offset of the newest row in the cache
+  u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
+  if (FUSED && p == parts - 1) {
+    const int unit_new = (nb - 1 - j0) / TPS;
+    if (wave == unit_new % kWaves) {
+      const int row_new = (L - 1) % BS;
+      i_new = unit_new / kWaves;
+      x_new = ((nb - 1 - j0) % TPS) * G::kLoads + row_new / G::kRpl;
+      lane_new = r == row_new % G::kRpl;
+      const int64_t src = row * G::kRowBytes + 16 * c;
+      kn = *reinterpret_cast<const u32x4*>(k_new + src);
+      vn = *reinterpret_cast<const u32x4*>(v_new + src);
+      const int32_t bl = block_tables[int64_t(s) * max_blocks + (L - 1) / BS];
+      if (static_cast<uint64_t>(static_cast<int64_t>(bl)) < static_cast<uint64_t>(num_blocks))
+        dst_new = ((int64_t(bl) * H + h) * BS + row_new) * G::kRowBytes + 16 * c;
+    }
+  }
 
   const u32x4 qv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(q) +
                                                    (row * D + c * G::kEpl) * G::kBytes);
@@ -343,6 +350,28 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
     m = m_new;
   };
 
+  // The newest row enters stage i_new from registers (see above).
+  auto put_newest = [&](u32x4* kb, u32x4* vb, int i) {
+    if (!FUSED || i != i_new) return;
+#pragma unroll
+    for (int x = 0; x < kRows; ++x) {
+      if (x == x_new && lane_new) {
+        kb[x] = kn;
+        vb[x] = vn;
+      }
+    }
+  };
+  // Its store to the cache, issued once the first stages' loads are in
+  // flight, so that the wait for the k_new / v_new loads overlaps them and the
+  // store has long completed when the wave ends.  Lanes of row 0 of the
+  // wave-wide load store the K row, lanes of row 1 the V row (every shape has
+  // at least 2 rows).
+  auto store_newest = [&]() {
+    if (!FUSED || dst_new < 0) return;
+    if (r == 0) *reinterpret_cast<u32x4*>(k_cache + dst_new) = kn;
+    else if (r == 1) *reinterpret_cast<u32x4*>(v_cache + dst_new) = vn;
+  };
+
   // NST-deep pipeline over register buffers: stage i + NST - 1's loads are
   // issued before stage i is consumed.  The body has no branch between a
   // buffer's loads and its consumer (steps past the wave's last stage consume
@@ -357,12 +386,15 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
       table_at(b, ids);
       issue(kb[b], vb[b], b, ids);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    store_newest();
     for (int i = 0; i < n_my; i += NST) {
 #pragma unroll
       for (int b = 0; b < NST; ++b) {
         table_at(i + b + NST - 1, ids);
         issue(kb[(b + NST - 1) % NST], vb[(b + NST - 1) % NST], i + b + NST - 1, ids);
         __builtin_amdgcn_sched_barrier(0);
+        put_newest(kb[b], vb[b], i + b);
         consume(kb[b], vb[b], i + b);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -447,7 +479,10 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(unsigned(a.num_heads), unsigned(a.partitions), unsigned(a.num_seqs));
   constexpr int kWaves = waves_for<BS>();
   constexpr int kTps = tiles_for<DT, D, BS>();
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, kWaves, kTps, stages_for<DT, kTps>()>), grid, dim3(64 * kWaves), 0, stream, a.q,
+  constexpr int kNst = stages_for<DT, kTps>();
+  auto* kernel = a.k_new != nullptr ? decode_partition_kernel<DT, D, BS, kWaves, kTps, kNst, true>
+                                    : decode_partition_kernel<DT, D, BS, kWaves, kTps, kNst, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(64 * kWaves), 0, stream, a.q,
                      static_cast<char*>(a.k_cache), static_cast<char*>(a.v_cache),
                      a.block_tables, a.context_lens, a.out, a.ws_m, a.ws_l, a.ws_acc, a.num_blocks,
                      a.max_blocks, a.part_blocks, a.partitions, a.scale_log2,
