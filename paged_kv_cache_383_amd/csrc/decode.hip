@@ -40,6 +40,8 @@
 // base-2 logits (scale * log2 e folded in) so exp is a single v_exp_f32.
 #include <hip/hip_fp16.h>
 
+#include <type_traits>
+
 #include "pagedkv.h"
 #include "pkv_internal.h"
 
@@ -327,7 +329,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
 #pragma unroll
     for (int u = 0; u < TPS; ++u) {
       const int j = first_block(i) + u;
-      const int ntok = (i < n_my && j < j1) ? L - j * BS : 0;   // rows at or past it are masked
+      const int ntok = (i >= 0 && i < n_my && j < j1) ? L - j * BS : 0;   // rows at or past it are masked
 #pragma unroll
       for (int t = 0; t < G::kLoads; ++t) {
         const int x = u * G::kLoads + t;
@@ -350,8 +352,17 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
     m = m_new;
   };
 
-  // The newest row enters stage i_new from registers (see above).
-  auto put_newest = [&](u32x4* kb, u32x4* vb, int i) {
+  // The newest row's store to the cache, issued without a wait.  Lanes of row
+  // 0 of the wave-wide load store the K row, lanes of row 1 the V row (every
+  // shape has at least 2 rows).
+  auto store_newest = [&]() {
+    if (!FUSED || dst_new < 0) return;
+    if (r == 0) *reinterpret_cast<u32x4*>(k_cache + dst_new) = kn;
+    else if (r == 1) *reinterpret_cast<u32x4*>(v_cache + dst_new) = vn;
+  };
+  // The newest row enters stage i_new from registers (see above); with
+  // STORE, its store is issued there too.
+  auto put_newest = [&](auto store, u32x4* kb, u32x4* vb, int i) {
     if (!FUSED || i != i_new) return;
 #pragma unroll
     for (int x = 0; x < kRows; ++x) {
@@ -360,43 +371,69 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
         vb[x] = vn;
       }
     }
+    if constexpr (decltype(store)::value) store_newest();
   };
-  // Its store to the cache, issued once the first stages' loads are in
-  // flight, so that the wait for the k_new / v_new loads overlaps them and the
-  // store has long completed when the wave ends.  Lanes of row 0 of the
-  // wave-wide load store the K row, lanes of row 1 the V row (every shape has
-  // at least 2 rows).
-  auto store_newest = [&]() {
-    if (!FUSED || dst_new < 0) return;
-    if (r == 0) *reinterpret_cast<u32x4*>(k_cache + dst_new) = kn;
-    else if (r == 1) *reinterpret_cast<u32x4*>(v_cache + dst_new) = vn;
-  };
+  using Store = std::true_type;
+  using NoStore = std::false_type;
 
-  // NST-deep pipeline over register buffers: stage i + NST - 1's loads are
-  // issued before stage i is consumed.  The body has no branch between a
-  // buffer's loads and its consumer (steps past the wave's last stage consume
-  // empty buffers, which leaves the state bit-for-bit unchanged), so the
-  // compiler cannot sink the loads below the consumer; the scheduling
-  // barriers keep the machine scheduler from doing the same inside a step.
+  // NST-deep pipeline over register buffers.  Step s issues the loads of
+  // stage s into buffer s % NST, then consumes stage s - (NST - 1), whose
+  // loads were issued NST - 1 steps earlier.  The body has no branch between
+  // a buffer's loads and its consumer, so the compiler cannot sink the loads
+  // below the consumer; the scheduling barriers keep the machine scheduler
+  // from doing the same inside a step.  Steps past the wave's last stage issue
+  // empty loads and consume empty buffers, which leaves the state bit-for-bit
+  // unchanged.
+  //
+  // Two ways to start it, equal in what they compute.  Without a prologue the
+  // first NST - 1 steps consume stages below 0 from zeroed buffers: every
+  // buffer is then written only inside the loop, and the register allocator
+  // keeps each one in the same registers across the back edge.  With the
+  // first NST - 1 stages issued in a prologue, it gave the V buffers other
+  // registers in the loop and copied them back on every iteration, which
+  // waits for every load in flight.  The prologue form (with the newest row's
+  // store right after the prologue, outside the loop) is kept only for the
+  // fused 3-stage kernel: it spills part of its ring to AGPRs, and in the
+  // prologue-free form the copies back from them wait for all loads on every
+  // iteration instead.
+  constexpr bool kPrologue = FUSED && NST > 2;
   if (n_my > 0) {
     u32x4 kb[NST][kRows], vb[NST][kRows];
     int32_t ids[TPS];
+    if constexpr (kPrologue) {
 #pragma unroll
-    for (int b = 0; b < NST - 1; ++b) {
-      table_at(b, ids);
-      issue(kb[b], vb[b], b, ids);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    store_newest();
-    for (int i = 0; i < n_my; i += NST) {
+      for (int b = 0; b < NST - 1; ++b) {
+        table_at(b, ids);
+        issue(kb[b], vb[b], b, ids);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      store_newest();
+      for (int i = 0; i < n_my; i += NST) {
 #pragma unroll
-      for (int b = 0; b < NST; ++b) {
-        table_at(i + b + NST - 1, ids);
-        issue(kb[(b + NST - 1) % NST], vb[(b + NST - 1) % NST], i + b + NST - 1, ids);
-        __builtin_amdgcn_sched_barrier(0);
-        put_newest(kb[b], vb[b], i + b);
-        consume(kb[b], vb[b], i + b);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int b = 0; b < NST; ++b) {
+          table_at(i + b + NST - 1, ids);
+          issue(kb[(b + NST - 1) % NST], vb[(b + NST - 1) % NST], i + b + NST - 1, ids);
+          __builtin_amdgcn_sched_barrier(0);
+          put_newest(NoStore{}, kb[b], vb[b], i + b);
+          consume(kb[b], vb[b], i + b);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NST; ++b)
+#pragma unroll
+        for (int x = 0; x < kRows; ++x) kb[b][x] = vb[b][x] = u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < n_my + NST - 1; i += NST) {
+#pragma unroll
+        for (int b = 0; b < NST; ++b) {
+          table_at(i + b, ids);
+          issue(kb[b], vb[b], i + b, ids);
+          __builtin_amdgcn_sched_barrier(0);
+          put_newest(Store{}, kb[(b + 1) % NST], vb[(b + 1) % NST], i + b - (NST - 1));
+          consume(kb[(b + 1) % NST], vb[(b + 1) % NST], i + b - (NST - 1));
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   }
