@@ -323,7 +323,12 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
 
   // Fold stage i into the row's running softmax state.
   constexpr int kRows = TPS * G::kLoads;                  // token rows per lane per stage
-  auto consume = [&](const u32x4* kb, const u32x4* vb, int i) {
+  // With SUB (the fused step's stage i_new only), the lanes of the newest row
+  // take it from registers (kn, vn) instead of the stage buffers.
+  auto consume = [&](auto sub, const u32x4* kb, const u32x4* vb, int i) {
+    constexpr bool kSub = decltype(sub)::value;
+    auto k_at = [&](int x) { return kSub && x == x_new && lane_new ? kn : kb[x]; };
+    auto v_at = [&](int x) { return kSub && x == x_new && lane_new ? vn : vb[x]; };
     float sc[kRows];
     float bm = kEmptyMax;
 #pragma unroll
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
 #pragma unroll
       for (int t = 0; t < G::kLoads; ++t) {
         const int x = u * G::kLoads + t;
-        const float d = row_sum<G::kLpr>(dot16<DT>(qv, kb[x])) * scale_log2;
+        const float d = row_sum<G::kLpr>(dot16<DT>(qv, k_at(x))) * scale_log2;
         sc[x] = (t * G::kRpl + r < ntok) ? d : -__builtin_inff();
         bm = fmaxf(bm, sc[x]);
       }
@@ -347,7 +352,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
     for (int x = 0; x < kRows; ++x) {
       const float pr = exp2_fast(sc[x] - m_new);
       l += pr;
-      axpy16<DT>(pr, vb[x], acc);
+      axpy16<DT>(pr, v_at(x), acc);
     }
     m = m_new;
   };
@@ -362,21 +367,21 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
     if (r == 0) __builtin_nontemporal_store(kn, reinterpret_cast<u32x4*>(k_cache + dst_new));
     else if (r == 1) __builtin_nontemporal_store(vn, reinterpret_cast<u32x4*>(v_cache + dst_new));
   };
-  // The newest row enters stage i_new from registers (see above); with
-  // STORE, its store is issued there too.
-  auto put_newest = [&](auto store, u32x4* kb, u32x4* vb, int i) {
-    if (!FUSED || i != i_new) return;
-#pragma unroll
-    for (int x = 0; x < kRows; ++x) {
-      if (x == x_new && lane_new) {
-        kb[x] = kn;
-        vb[x] = vn;
-      }
+  // Fold stage i into the state; the fused step's stage i_new takes the
+  // newest row from registers (see above), and with STORE its store to the
+  // cache is issued there too.  Only that one stage of one wave takes the
+  // substituting branch: the stage buffers are never written outside their
+  // loads, so the common path needs no copies of them.
+  using Yes = std::true_type;
+  using No = std::false_type;
+  auto fold = [&](auto store, const u32x4* kb, const u32x4* vb, int i) {
+    if (FUSED && i == i_new) {
+      consume(Yes{}, kb, vb, i);
+      if constexpr (decltype(store)::value) store_newest();
+    } else {
+      consume(No{}, kb, vb, i);
     }
-    if constexpr (decltype(store)::value) store_newest();
   };
-  using Store = std::true_type;
-  using NoStore = std::false_type;
 
   // NST-deep pipeline over register buffers.  Step s issues the loads of
   // stage s into buffer s % NST, then consumes stage s - (NST - 1), whose
@@ -416,8 +421,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
           table_at(i + b + NST - 1, ids);
           issue(kb[(b + NST - 1) % NST], vb[(b + NST - 1) % NST], i + b + NST - 1, ids);
           __builtin_amdgcn_sched_barrier(0);
-          put_newest(NoStore{}, kb[b], vb[b], i + b);
-          consume(kb[b], vb[b], i + b);
+          fold(No{}, kb[b], vb[b], i + b);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -432,8 +436,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
           table_at(i + b, ids);
           issue(kb[b], vb[b], i + b, ids);
           __builtin_amdgcn_sched_barrier(0);
-          put_newest(Store{}, kb[(b + 1) % NST], vb[(b + 1) % NST], i + b - (NST - 1));
-          consume(kb[(b + 1) % NST], vb[(b + 1) % NST], i + b - (NST - 1));
+          fold(Yes{}, kb[(b + 1) % NST], vb[(b + 1) % NST], i + b - (NST - 1));
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -443,7 +446,13 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
   // Merge the kStates row states of the work-group.
   __shared__ float sm_m[G::kStates];
   __shared__ float sm_l[G::kStates];
-  __shared__ float sm_acc[G::kStates * D];
+  // The 3-deep ring of 32-token tiles runs one 4-wave work-group per compute
+  // unit: with two (the fused kernel's registers allow it) it measured 3 %
+  // slower.  The merge buffer is sized past half of the compute unit's
+  // 160 KiB of LDS, which leaves no room for a second work-group.
+  constexpr int kAccFloats = G::kStates * D;
+  constexpr int kOneGroupFloats = NST > 2 ? 96 * 1024 / 4 : 0;
+  __shared__ float sm_acc[kAccFloats > kOneGroupFloats ? kAccFloats : kOneGroupFloats];
   __shared__ int sm_bad[kWaves];
   const int st = wave * G::kRpl + r;
   if (c == 0) {
