@@ -40,8 +40,6 @@
 // base-2 logits (scale * log2 e folded in) so exp is a single v_exp_f32.
 #include <hip/hip_fp16.h>
 
-#include <type_traits>
-
 #include "pagedkv.h"
 #include "pkv_internal.h"
 
@@ -242,29 +240,28 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
   // cache and PagedAttention explained", Step 6: the decode token's K/V goes
   // to the next slot of the sequence's last block).  Only one wave of one
   // work-group per (sequence, head) reads that block: the wave of the last
-  // partition whose stages hold block nb - 1.  That wave takes the new row's
-  // 16-byte column c straight from k_new / v_new into registers here, puts it
-  // in place of the cache row when it consumes the stage, and stores it to
-  // the cache without waiting for the store: no load of this launch depends
-  // on it.  The values used are the same bits a write-then-read would return.
+  // partition whose stages hold block nb - 1.  That wave stores the row here,
+  // before its loop (lanes of row 0 of a wave-wide load move the K row, lanes
+  // of row 1 the V row; every shape has at least 2 rows), and waits for the
+  // store only right before it issues the loads of stage i_new, the one
+  // holding that block (see await_newest): in all but the shortest rows the
+  // store has long completed by then.  The loop itself is the plain decode's,
+  // with nothing held across it, so the fused kernel needs no more registers
+  // than the plain one.  The stage then reads the stored bits, exactly what a
+  // write followed by a decode reads.
   int i_new = -1;                                         // stage index holding the newest row (owner wave)
-  int x_new = 0;                                          // its row slot within the stage buffers
-  bool lane_new = false;                                  // this lane holds a column of the newest row
-  int64_t dst_new = -1;                                   // byte offset of the newest row in the cache
-  u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
   if (FUSED && p == parts - 1) {
     const int unit_new = (nb - 1 - j0) / TPS;
     if (wave == unit_new % kWaves) {
-      const int row_new = (L - 1) % BS;
       i_new = unit_new / kWaves;
-      x_new = ((nb - 1 - j0) % TPS) * G::kLoads + row_new / G::kRpl;
-      lane_new = r == row_new % G::kRpl;
-      const int64_t src = row * G::kRowBytes + 16 * c;
-      kn = *reinterpret_cast<const u32x4*>(k_new + src);
-      vn = *reinterpret_cast<const u32x4*>(v_new + src);
       const int32_t bl = block_tables[int64_t(s) * max_blocks + (L - 1) / BS];
-      if (static_cast<uint64_t>(static_cast<int64_t>(bl)) < static_cast<uint64_t>(num_blocks))
-        dst_new = ((int64_t(bl) * H + h) * BS + row_new) * G::kRowBytes + 16 * c;
+      if (static_cast<uint64_t>(static_cast<int64_t>(bl)) < static_cast<uint64_t>(num_blocks) && r < 2) {
+        const int64_t src = row * G::kRowBytes + 16 * c;
+        const int64_t dst = ((int64_t(bl) * H + h) * BS + (L - 1) % BS) * G::kRowBytes + 16 * c;
+        const char* from = r == 0 ? k_new : v_new;
+        char* to = r == 0 ? k_cache : v_cache;
+        *reinterpret_cast<u32x4*>(to + dst) = *reinterpret_cast<const u32x4*>(from + src);
+      }
     }
   }
 
@@ -323,12 +320,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
 
   // Fold stage i into the row's running softmax state.
   constexpr int kRows = TPS * G::kLoads;                  // token rows per lane per stage
-  // With SUB (the fused step's stage i_new only), the lanes of the newest row
-  // take it from registers (kn, vn) instead of the stage buffers.
-  auto consume = [&](auto sub, const u32x4* kb, const u32x4* vb, int i) {
-    constexpr bool kSub = decltype(sub)::value;
-    auto k_at = [&](int x) { return kSub && x == x_new && lane_new ? kn : kb[x]; };
-    auto v_at = [&](int x) { return kSub && x == x_new && lane_new ? vn : vb[x]; };
+  auto consume = [&](const u32x4* kb, const u32x4* vb, int i) {
     float sc[kRows];
     float bm = kEmptyMax;
 #pragma unroll
@@ -338,7 +330,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
 #pragma unroll
       for (int t = 0; t < G::kLoads; ++t) {
         const int x = u * G::kLoads + t;
-        const float d = row_sum<G::kLpr>(dot16<DT>(qv, k_at(x))) * scale_log2;
+        const float d = row_sum<G::kLpr>(dot16<DT>(qv, kb[x])) * scale_log2;
         sc[x] = (t * G::kRpl + r < ntok) ? d : -__builtin_inff();
         bm = fmaxf(bm, sc[x]);
       }
@@ -352,93 +344,53 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
     for (int x = 0; x < kRows; ++x) {
       const float pr = exp2_fast(sc[x] - m_new);
       l += pr;
-      axpy16<DT>(pr, v_at(x), acc);
+      axpy16<DT>(pr, vb[x], acc);
     }
     m = m_new;
   };
 
-  // The newest row's store to the cache, issued without a wait and marked
-  // non-temporal (nothing in this launch reads it back; measured 0.3-0.5 %
-  // faster steps than the default policy).  Lanes of row 0 of the wave-wide
-  // load store the K row, lanes of row 1 the V row (every shape has at least
-  // 2 rows).
-  auto store_newest = [&]() {
-    if (!FUSED || dst_new < 0) return;
-    if (r == 0) __builtin_nontemporal_store(kn, reinterpret_cast<u32x4*>(k_cache + dst_new));
-    else if (r == 1) __builtin_nontemporal_store(vn, reinterpret_cast<u32x4*>(v_cache + dst_new));
-  };
-  // Fold stage i into the state; the fused step's stage i_new takes the
-  // newest row from registers (see above), and with STORE its store to the
-  // cache is issued there too.  Only that one stage of one wave takes the
-  // substituting branch: the stage buffers are never written outside their
-  // loads, so the common path needs no copies of them.
-  using Yes = std::true_type;
-  using No = std::false_type;
-  auto fold = [&](auto store, const u32x4* kb, const u32x4* vb, int i) {
-    if (FUSED && i == i_new) {
-      consume(Yes{}, kb, vb, i);
-      if constexpr (decltype(store)::value) store_newest();
-    } else {
-      consume(No{}, kb, vb, i);
-    }
+  // Before the owner wave issues the loads of stage i_new, every memory
+  // operation older than the last NST - 1 stages' loads has completed, the
+  // newest row's store among them (vector memory operations retire in order
+  // on gfx9, stores included).  For any other stage, and any other wave, this
+  // is not reached.
+  constexpr int kLoadsPerStage = 2 * TPS * G::kLoads;
+  constexpr int kAwait = (NST - 1) * kLoadsPerStage;
+  static_assert(kAwait < 64, "vmcnt holds 6 bits");
+  auto await_newest = [&](int i) {
+    if (FUSED && i == i_new)
+      __builtin_amdgcn_s_waitcnt((kAwait & 15) | ((kAwait >> 4) << 14) | (7 << 4) | (15 << 8));
   };
 
   // NST-deep pipeline over register buffers.  Step s issues the loads of
   // stage s into buffer s % NST, then consumes stage s - (NST - 1), whose
-  // loads were issued NST - 1 steps earlier.  The body has no branch between
-  // a buffer's loads and its consumer, so the compiler cannot sink the loads
-  // below the consumer; the scheduling barriers keep the machine scheduler
-  // from doing the same inside a step.  Steps past the wave's last stage issue
-  // empty loads and consume empty buffers, which leaves the state bit-for-bit
-  // unchanged.
-  //
-  // Two ways to start it, equal in what they compute.  Without a prologue the
-  // first NST - 1 steps consume stages below 0 from zeroed buffers: every
-  // buffer is then written only inside the loop, and the register allocator
-  // keeps each one in the same registers across the back edge.  With the
-  // first NST - 1 stages issued in a prologue, it gave the V buffers other
-  // registers in the loop and copied them back on every iteration, which
-  // waits for every load in flight.  The prologue form (with the newest row's
-  // store right after the prologue, outside the loop) is kept only for the
-  // fused 3-stage kernel: it spills part of its ring to AGPRs, and in the
-  // prologue-free form the copies back from them wait for all loads on every
-  // iteration instead.
-  constexpr bool kPrologue = FUSED && NST > 2;
+  // loads were issued NST - 1 steps earlier.  The first NST - 1 steps consume
+  // stages below 0 from zeroed buffers and steps past the wave's last stage
+  // issue empty loads; both leave the state bit-for-bit unchanged.  There is
+  // no prologue: every buffer is written only inside the loop, so the
+  // register allocator keeps each one in the same registers across the back
+  // edge (with a prologue it gave the V buffers other registers there and
+  // copied them, which forced a wait for every load in flight once per
+  // iteration).  The body has no branch between a buffer's loads and its
+  // consumer, so the compiler cannot sink the loads below the consumer; the
+  // scheduling barriers keep the machine scheduler from doing the same
+  // inside a step.
   if (n_my > 0) {
     u32x4 kb[NST][kRows], vb[NST][kRows];
+#pragma unroll
+    for (int b = 0; b < NST; ++b)
+#pragma unroll
+      for (int x = 0; x < kRows; ++x) kb[b][x] = vb[b][x] = u32x4{0u, 0u, 0u, 0u};
     int32_t ids[TPS];
-    if constexpr (kPrologue) {
+    for (int i = 0; i < n_my + NST - 1; i += NST) {
 #pragma unroll
-      for (int b = 0; b < NST - 1; ++b) {
-        table_at(b, ids);
-        issue(kb[b], vb[b], b, ids);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      store_newest();
-      for (int i = 0; i < n_my; i += NST) {
-#pragma unroll
-        for (int b = 0; b < NST; ++b) {
-          table_at(i + b + NST - 1, ids);
-          issue(kb[(b + NST - 1) % NST], vb[(b + NST - 1) % NST], i + b + NST - 1, ids);
-          __builtin_amdgcn_sched_barrier(0);
-          fold(No{}, kb[b], vb[b], i + b);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < NST; ++b)
-#pragma unroll
-        for (int x = 0; x < kRows; ++x) kb[b][x] = vb[b][x] = u32x4{0u, 0u, 0u, 0u};
-      for (int i = 0; i < n_my + NST - 1; i += NST) {
-#pragma unroll
-        for (int b = 0; b < NST; ++b) {
-          table_at(i + b, ids);
-          issue(kb[b], vb[b], i + b, ids);
-          __builtin_amdgcn_sched_barrier(0);
-          fold(Yes{}, kb[(b + 1) % NST], vb[(b + 1) % NST], i + b - (NST - 1));
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int b = 0; b < NST; ++b) {
+        table_at(i + b, ids);
+        await_newest(i + b);
+        issue(kb[b], vb[b], i + b, ids);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(kb[(b + 1) % NST], vb[(b + 1) % NST], i + b - (NST - 1));
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -447,9 +399,10 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
   __shared__ float sm_m[G::kStates];
   __shared__ float sm_l[G::kStates];
   // The 3-deep ring of 32-token tiles runs one 4-wave work-group per compute
-  // unit: with two (the fused kernel's registers allow it) it measured 3 %
-  // slower.  The merge buffer is sized past half of the compute unit's
-  // 160 KiB of LDS, which leaves no room for a second work-group.
+  // unit: with two (a version of the fused kernel whose registers allowed it)
+  // it measured 3 % slower.  Its registers alone keep it to one today; the
+  // merge buffer is also sized past half of the compute unit's 160 KiB of
+  // LDS, so that stays true whatever the register count.
   constexpr int kAccFloats = G::kStates * D;
   constexpr int kOneGroupFloats = NST > 2 ? 96 * 1024 / 4 : 0;
   __shared__ float sm_acc[kAccFloats > kOneGroupFloats ? kAccFloats : kOneGroupFloats];
