@@ -349,17 +349,27 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
     m = m_new;
   };
 
-  // Before the owner wave issues the loads of stage i_new, every memory
-  // operation older than the last NST - 1 stages' loads has completed, the
-  // newest row's store among them (vector memory operations retire in order
-  // on gfx9, stores included).  For any other stage, and any other wave, this
-  // is not reached.
+  // Before the owner wave issues the loads of stage i_new, the newest row's
+  // store has completed.  Vector memory operations retire in order on gfx9,
+  // stores included, and the store is older than every stage load, so it is
+  // enough to wait until no more than the loads of the stages issued since
+  // are outstanding: min(i, NST - 1) stages (later ones than that have been
+  // consumed, hence waited for, already).  For i = 0 nothing has been issued
+  // since, and the wait is for everything.  For any other stage, and any
+  // other wave, this is not reached.
   constexpr int kLoadsPerStage = 2 * TPS * G::kLoads;
-  constexpr int kAwait = (NST - 1) * kLoadsPerStage;
-  static_assert(kAwait < 64, "vmcnt holds 6 bits");
+  static_assert(NST <= 3 && (NST - 1) * kLoadsPerStage < 64, "vmcnt holds 6 bits; cases below cover NST <= 3");
   auto await_newest = [&](int i) {
-    if (FUSED && i == i_new)
-      __builtin_amdgcn_s_waitcnt((kAwait & 15) | ((kAwait >> 4) << 14) | (7 << 4) | (15 << 8));
+    if (FUSED && i == i_new) {
+      constexpr int kOthers = (7 << 4) | (15 << 8);            // expcnt, lgkmcnt: no wait
+      constexpr auto vm = [](int n) { return (n & 15) | ((n >> 4) << 14); };
+      if (i == 0)
+        __builtin_amdgcn_s_waitcnt(vm(0) | kOthers);
+      else if (NST > 2 && i == 1)
+        __builtin_amdgcn_s_waitcnt(vm(kLoadsPerStage) | kOthers);
+      else
+        __builtin_amdgcn_s_waitcnt(vm((NST - 1) * kLoadsPerStage) | kOthers);
+    }
   };
 
   // NST-deep pipeline over register buffers.  Step s issues the loads of
