@@ -183,6 +183,38 @@ def copy_calibration(mib):
                       "launches": 5}), flush=True)
 
 
+def torch_stream_reference(reps=20):
+    """Plain PyTorch streaming on the same GPU, timed the same way, to read the decode's roofline fraction
+    against: a 1 GiB fp32 elementwise copy (torch.neg: reads 1 GiB, writes 1 GiB) and a read-only sum over
+    2 GiB. Both buffers are far larger than the caches. A diagnostic only: not the library's path."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    big = torch.ones(2 * n, dtype=torch.float32, device="cuda:0")
+    for _ in range(3):
+        torch.neg(src, out=dst)
+        big.sum()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_s = e0.elapsed_time(e1) / 1e3 / reps
+    e0.record()
+    for _ in range(reps):
+        big.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    sum_s = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst, big
+    torch.cuda.empty_cache()
+    return {"torch_copy_1GiB_GBps": round(2 * n * 4 / copy_s / 1e9, 1),
+            "torch_sum_2GiB_read_GBps": round(2 * n * 4 / sum_s / 1e9, 1),
+            "note": "plain PyTorch streaming on the same GPU (torch.neg copy, torch.sum read), events"}
+
+
 def parallel_sampling(args):
     """Decode step of parallel sampling over shared prompts: the block pool reserves each sample's new
     slot (copying the shared, partly filled last block of a prompt for all but its last writer), then
@@ -685,6 +717,9 @@ def main():
         f"{graph_us:.1f} us), decode {decode_us:.1f} us, "
         f"write {write_us:.1f} us -> decode {achieved:.0f} GB/s = {achieved / PEAK_HBM_GBS:.1%} of peak")
 
+    stream_ref = torch_stream_reference()
+    log(f"plain PyTorch streaming on this GPU: {stream_ref}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the same workload ...")
@@ -739,6 +774,7 @@ def main():
             "algorithmic_bytes_per_launch": nbytes["decode"],
             "mean_launch_us": round(decode_us, 2),
         },
+        "diagnostic": stream_ref,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
