@@ -250,9 +250,9 @@ int paged_kv_prepare_step(int32_t* block_tables, int32_t max_blocks_per_seq, int
  * token's K/V goes to the next slot of its last block) followed by
  * paged_attention_decode with the same arguments: same results, bit for bit.
  * Within the launch, the one wave of each (sequence, head) that reads the
- * block of position L - 1 takes that row from k_new / v_new in place of the
- * cache row and stores it to the cache; nothing in the launch reads the slot
- * back.  Rows with L = 0 append nothing and are zero.
+ * block of position L - 1 first stores that row from k_new / v_new into its
+ * slot, and reads the block only once the store has completed.  Rows with
+ * L = 0 append nothing and are zero.
  *
  *   k_new, v_new  [num_seqs, num_heads, head_dim], dtype, read
  *   k_cache,
