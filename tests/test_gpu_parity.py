@@ -118,6 +118,13 @@ def test_decode_step_matches_oracle(pkv, cfg_id):
                         cfg.block_size, cfg.dtype, seqs=seqs)
     err, rel = check_close(got[seqs], ref[seqs], cfg.dtype, f"config {cfg_id}")
     say(f"  max-abs {err:.3e} rel-L2 {rel:.3e}")
+    # the launch the benchmark times: the fused step at the library's own split (its store of the newest
+    # rows rewrites the values already written above)
+    fused = out_host(pkv.paged_attention_decode_step(w.q, w.k_new, w.v_new, w.k_cache, w.v_cache, w.block_tables,
+                                                     w.context_lens, cfg.scale, partition_size=pkv.PARTITION_AUTO))
+    err_f, rel_f = check_close(fused[seqs], ref[seqs], cfg.dtype, f"config {cfg_id} fused step, automatic split")
+    say(f"  fused step, automatic split: max-abs {err_f:.3e} rel-L2 {rel_f:.3e}")
+    assert np.all(np.isfinite(fused))
     # every row, sampled or not: finite and inside the convex hull bounds of its values
     assert np.all(np.isfinite(got))
     if len(seqs) < len(meta.context_lens):
