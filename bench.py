@@ -236,8 +236,7 @@ def parallel_sampling(args):
         pool = pkv.BlockPool(nb, bs, order)
         gen = torch.Generator(device=dev)
         gen.manual_seed(cfg.seed + r)
-        kc = torch.empty((nb, H, bs, D), dtype=dt, device=dev)
-        vc = torch.empty_like(kc)
+        kc, vc = W.kv_pool(nb, H, bs, D, dt, dev)
         W._randn_into(kc, gen, 1.0, 1024)
         W._randn_into(vc, gen, 1.0, 1024)
         seqs, slots, copies = [], [], []
@@ -364,8 +363,7 @@ def continuous_batching(args):
     NB = R * cfg.width                         # every row can reach its longest request: no preemption
     gen = torch.Generator(device=dev)
     gen.manual_seed(cfg.seed)
-    kc = torch.empty((NB, H, bs, D), dtype=dt, device=dev)
-    vc = torch.empty_like(kc)
+    kc, vc = W.kv_pool(NB, H, bs, D, dt, dev)
     W._randn_into(kc, gen, 1.0, 512)
     W._randn_into(vc, gen, 1.0, 512)
     src_k = torch.randn((cfg.prompt_max, H, D), generator=gen, device=dev).to(dt)
@@ -494,8 +492,7 @@ def prefill(args):
                             for i, L in enumerate(lens.tolist())]).astype(np.int64)
     gen = torch.Generator(device=dev)
     gen.manual_seed(cfg.seed)
-    kc = torch.zeros((nb, H, bs, D), dtype=dt, device=dev)
-    vc = torch.zeros_like(kc)
+    kc, vc = W.kv_pool(nb, H, bs, D, dt, dev, zero=True)
     kp = torch.randn((T, H, D), generator=gen, device=dev).to(dt)
     vp = torch.randn((T, H, D), generator=gen, device=dev).to(dt)
     q = torch.randn((T, H, D), generator=gen, device=dev).to(dt)
