@@ -97,3 +97,20 @@ def test_secondary_workloads_are_seeded_and_well_formed():
     pc = W.PrefillConfig()
     lens, nb, order = W.prefill_prompts(pc)
     assert len(lens) == pc.prompts and nb == -(-5 * int(((lens + 15) // 16).sum()) // 4)
+
+
+def test_kv_pool_is_one_allocation_with_v_after_k():
+    """The generators hold a layer's K and V caches as the two halves of one tensor (V directly after K), the
+    placement the decode measured fastest; each half is a contiguous [NB, H, bs, D] cache."""
+    torch = pytest.importorskip("torch")
+    for zero in (False, True):
+        k, v = W.kv_pool(7, 3, 16, 64, torch.bfloat16, "cpu", zero=zero)
+        assert k.shape == v.shape == (7, 3, 16, 64) and k.is_contiguous() and v.is_contiguous()
+        assert k.untyped_storage().data_ptr() == v.untyped_storage().data_ptr()
+        assert v.data_ptr() - k.data_ptr() == k.numel() * k.element_size()
+        if zero:
+            assert not k.any() and not v.any()
+    meta = W.make_metadata(1)
+    w = W.make_workload(meta, "cpu")
+    assert w.v_cache.data_ptr() - w.k_cache.data_ptr() == w.k_cache.numel() * w.k_cache.element_size()
+
