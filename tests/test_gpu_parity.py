@@ -222,6 +222,44 @@ def test_fused_step_edge_lengths_every_shape(pkv, dt, D, bs):
         check_close(out_host(out_b), ref, c.dtype, f"fused {dt} D{D} bs{bs} part{part}")
 
 
+@pytest.mark.parametrize("dt,D,bs", SHAPES, ids=[f"{a}-d{b}-bs{c}" for a, b, c in SHAPES])
+def test_random_small_batches_fused_and_plain(pkv, dt, D, bs):
+    """Seeded random batches (batch size, head count, lengths, split) for every shape: the fused step equals
+    paged_kv_write + paged_attention_decode bit for bit, and both match the oracle."""
+    rng = np.random.default_rng(3000 + 7 * D + bs + {"f32": 0, "f16": 1, "bf16": 2}[dt])
+    vi = torch.int32 if dt == "f32" else torch.int16
+    for trial in range(4):
+        B = int(rng.integers(1, 24))
+        H = int(rng.integers(1, 7))
+        lens = [int(x) for x in rng.integers(1, 9 * bs + 1, B)]
+        part = [0, bs, 2 * bs, 4 * bs, 512, pkv.PARTITION_AUTO][int(rng.integers(0, 6))]
+        say(f"[random] {dt} D={D} bs={bs} trial {trial}: B={B} H={H} partition={part} lens={lens}")
+        c = P.Case(rng, lens, H=H, D=D, bs=bs, dtype="bf16" if dt == "bf16" else dt)
+        ref = oracle.decode(c.q, c.k_pool, c.v_pool, c.tables, c.context_lens, c.scale, bs, c.dtype)
+        k_new = np.stack([c.Klog[i][L - 1] for i, L in enumerate(lens)])
+        v_new = np.stack([c.Vlog[i][L - 1] for i, L in enumerate(lens)])
+        slots = np.array([int(c.tables[i, (L - 1) // bs]) * bs + (L - 1) % bs for i, L in enumerate(lens)],
+                         dtype=np.int64)
+        k_pool, v_pool = c.k_pool.copy(), c.v_pool.copy()
+        poison = np.uint16(0x7FC0) if c.dtype == "bf16" else k_pool.dtype.type(np.nan)
+        for i, L in enumerate(lens):
+            k_pool[c.tables[i, (L - 1) // bs], :, (L - 1) % bs, :] = poison
+            v_pool[c.tables[i, (L - 1) // bs], :, (L - 1) % bs, :] = poison
+        q = dev_tensor(c.q, c.dtype)
+        kn, vn = dev_tensor(k_new, c.dtype), dev_tensor(v_new, c.dtype)
+        tab = torch.from_numpy(c.tables).cuda()
+        lens_t = torch.from_numpy(c.context_lens).cuda()
+        ka, va = dev_tensor(k_pool, c.dtype), dev_tensor(v_pool, c.dtype)
+        kb, vb = dev_tensor(k_pool, c.dtype), dev_tensor(v_pool, c.dtype)
+        pkv.paged_kv_write(kn, vn, torch.from_numpy(slots).cuda(), ka, va)
+        out_a = pkv.paged_attention_decode(q, ka, va, tab, lens_t, c.scale, partition_size=part)
+        out_b = pkv.paged_attention_decode_step(q, kn, vn, kb, vb, tab, lens_t, c.scale, partition_size=part)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a.view(vi), out_b.view(vi)), trial
+        assert torch.equal(ka.view(vi), kb.view(vi)) and torch.equal(va.view(vi), vb.view(vi)), trial
+        check_close(out_host(out_b), ref, c.dtype, f"random {dt} D{D} bs{bs} trial {trial}")
+
+
 def test_split_and_single_pass_agree_long_context(pkv):
     """32k-token contexts: 512-token partitions + LSE merge vs one pass vs fine partitions."""
     rng = np.random.default_rng(77)
