@@ -64,11 +64,36 @@ def algorithmic_bytes(meta):
     return {"decode": decode, "write": write, "step": decode + write, "kv": kv}
 
 
-def cpu_baseline(meta, w, budget_s=10.0):
-    """The oracle, untouched, on the same workload: whole steps (write, then decode of sequence after
-    sequence) until about budget_s of CPU work; a step cut short counts only its finished sequences."""
-    import numpy as np
+CPU_MAX_WORKERS = 16           # one GPU's share of the host's cores
+
+
+def cpu_workers():
+    """Threads for the CPU oracle: the cores this process may run on, at most CPU_MAX_WORKERS."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, CPU_MAX_WORKERS))
+
+
+def cpu_host_info():
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return {"host_cpus": os.cpu_count(), "affinity_cpus": affinity}
+
+
+def cpu_baseline(meta, w, budget_s=12.0, single_s=4.0):
+    """The oracle, untouched, on the same workload and the host's cores.  Whole steps: the oracle's write of
+    the batch's new tokens (a copy of the whole pool), then oracle.decode of every sequence, the sequences
+    shared out to a pool of threads (one per core of this process's CPU share, at most 16; NumPy releases the
+    GIL inside the oracle's array operations), until about budget_s.  Then, for comparison, sequence after
+    sequence on one thread for about single_s."""
     import resource
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
 
     import oracle
     import workloads as W
@@ -81,60 +106,97 @@ def cpu_baseline(meta, w, budget_s=10.0):
     H, D, bs = cfg.num_heads, cfg.head_dim, cfg.block_size
     L = meta.context_lens.astype(np.int64)
     per_seq = L * H * D * 2 * es + H * D * 2 * es + 4 * ((L + bs - 1) // bs) + 4 + 2 * H * D * es * 2 + 8
-    nbytes, tokens, steps, seqs = 0, 0, 0, 0
+    order = np.argsort(-L, kind="stable").tolist()          # longest first: the pool's tail stays short
+    nw = cpu_workers()
+
+    def one(args):
+        kc, vc, i = args
+        oracle.decode(q, kc, vc, meta.block_tables, meta.context_lens, cfg.scale, bs, cfg.dtype, seqs=[i])
+        return i
+
+    nbytes, tokens, steps = 0, 0, 0
     cpu0 = resource.getrusage(resource.RUSAGE_SELF)
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        kc, vc = oracle.kv_write(kn, vn, meta.slot_mapping, k0, v0, cfg.block_size)
-        for i in range(B):
-            oracle.decode(q, kc, vc, meta.block_tables, meta.context_lens, cfg.scale, bs, cfg.dtype, seqs=[i])
-            nbytes += int(per_seq[i])
-            tokens += int(L[i]) * H
-            seqs += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        steps += 1
+    with ThreadPoolExecutor(nw) as ex:
+        while steps == 0 or time.perf_counter() - t0 < budget_s:
+            kc, vc = oracle.kv_write(kn, vn, meta.slot_mapping, k0, v0, cfg.block_size)
+            for i in ex.map(one, [(kc, vc, i) for i in order]):
+                nbytes += int(per_seq[i])
+                tokens += int(L[i]) * H
+            steps += 1
     wall = time.perf_counter() - t0
     cpu1 = resource.getrusage(resource.RUSAGE_SELF)
     cpu = (cpu1.ru_utime - cpu0.ru_utime) + (cpu1.ru_stime - cpu0.ru_stime)
-    return {"value": round(nbytes / wall / 1e9, 4), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
-            "kind": "oracle",
-            "sample": f"{seqs} sequence decodes over {steps} step(s) of the same {B}-sequence batch, each step "
-                      f"starting with the oracle's write of the {B} new tokens (a whole-pool copy); "
-                      f"{wall:.1f} s wall, {cpu:.1f} s CPU",
-            "tokens_heads_per_s": round(tokens / wall, 1)}
+    # one thread, for comparison: the decode of sequence after sequence (the write excluded)
+    sb, st, sn = 0, 0, 0
+    t1 = time.perf_counter()
+    del k0, v0
+    for i in order:
+        one((kc, vc, i))
+        sb += int(per_seq[i])
+        st += int(L[i]) * H
+        sn += 1
+        if time.perf_counter() - t1 >= single_s:
+            break
+    single_wall = time.perf_counter() - t1
+    return {"value": round(nbytes / wall / 1e9, 4), "unit": "GB/s", "cores": nw, "kind": "oracle",
+            "sample": f"{steps} whole step(s) of the {B}-sequence batch, each the oracle's write of the {B} new "
+                      f"tokens (a whole-pool copy) and then every sequence's decode on {nw} threads; "
+                      f"{wall:.1f} s wall, {cpu:.1f} s CPU ({cpu / wall:.1f} cores busy on average)",
+            "tokens_heads_per_s": round(tokens / wall, 1),
+            "single_thread": {"value": round(sb / single_wall / 1e9, 4), "unit": "GB/s",
+                              "tokens_heads_per_s": round(st / single_wall, 1),
+                              "sample": f"decode of the {sn} longest sequences one after another, "
+                                        f"{single_wall:.1f} s (no write)"},
+            **cpu_host_info()}
 
 
-def cpu_baseline_prefill(q, kc, vc, tables, lens, scale, bs, dtype, budget_s=10.0):
-    """The oracle's prefill, untouched, on the same prompts: one prompt after another (its queries over its own
-    cache blocks) until about budget_s; only finished prompts count."""
-    import numpy as np
+def cpu_baseline_prefill(q, kc, vc, tables, lens, scale, bs, dtype, budget_s=12.0):
+    """The oracle's prefill, untouched, on the same prompts and the host's cores: each prompt's queries over its
+    own cache blocks, prompts shared out to a pool of threads (as for the decode baseline), new prompts
+    started until about budget_s; the prompts still running then finish and count."""
     import resource
+    from concurrent.futures import FIRST_COMPLETED, ThreadPoolExecutor, wait
+
+    import numpy as np
 
     import oracle
     import workloads as W
     qh, kh, vh = W.storage_numpy(q), W.storage_numpy(kc), W.storage_numpy(vc)
     H, D = qh.shape[1], qh.shape[2]
     starts = np.concatenate([[0], np.cumsum(lens)])
+    nw = cpu_workers()
+
+    def one(i):
+        P = int(lens[i])
+        oracle.prefill(qh[starts[i]:starts[i] + P], kh, vh, tables[i:i + 1], np.array([0, P]), np.array([P]),
+                       scale, bs, dtype)
+        return i
+
     tokens, pairs, done = 0, 0, 0
     cpu0 = resource.getrusage(resource.RUSAGE_SELF)
     t0 = time.perf_counter()
-    for i, P in enumerate(lens.tolist()):
-        if time.perf_counter() - t0 >= budget_s:
-            break
-        oracle.prefill(qh[starts[i]:starts[i] + P], kh, vh, tables[i:i + 1], np.array([0, P]), np.array([P]),
-                       scale, bs, dtype)
-        tokens += P
-        pairs += P * (P + 1) // 2
-        done += 1
+    with ThreadPoolExecutor(nw) as ex:
+        pending, nxt = set(), 0
+        while nxt < len(lens) or pending:
+            while nxt < len(lens) and len(pending) < nw and time.perf_counter() - t0 < budget_s:
+                pending.add(ex.submit(one, nxt))
+                nxt += 1
+            if not pending:
+                break
+            finished, pending = wait(pending, return_when=FIRST_COMPLETED)
+            for f in finished:
+                P = int(lens[f.result()])
+                tokens += P
+                pairs += P * (P + 1) // 2
+                done += 1
     wall = time.perf_counter() - t0
     cpu1 = resource.getrusage(resource.RUSAGE_SELF)
     cpu = (cpu1.ru_utime - cpu0.ru_utime) + (cpu1.ru_stime - cpu0.ru_stime)
-    return {"value": round(tokens / wall, 1), "unit": "prompt tokens/s", "cores": max(1, round(cpu / wall)),
-            "kind": "oracle",
-            "sample": f"{done} of the {len(lens)} prompts ({tokens} tokens), each prefilled alone; "
-                      f"{wall:.1f} s wall, {cpu:.1f} s CPU",
-            "tflops": round(pairs * H * 4 * D / wall / 1e12, 6)}
+    return {"value": round(tokens / wall, 1), "unit": "prompt tokens/s", "cores": nw, "kind": "oracle",
+            "sample": f"{done} of the {len(lens)} prompts ({tokens} tokens), shortest first, each prefilled alone, "
+                      f"on {nw} threads; {wall:.1f} s wall, {cpu:.1f} s CPU ({cpu / wall:.1f} cores busy on average)",
+            "tflops": round(pairs * H * 4 * D / wall / 1e12, 6), **cpu_host_info()}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partition_llama13b_b64_hbm_traffic.md")
@@ -213,6 +275,63 @@ def torch_stream_reference(reps=20):
     return {"torch_copy_1GiB_GBps": round(2 * n * 4 / copy_s / 1e9, 1),
             "torch_sum_2GiB_read_GBps": round(2 * n * 4 / sum_s / 1e9, 1),
             "note": "plain PyTorch streaming on the same GPU (torch.neg copy, torch.sum read), events"}
+
+
+def read_ceiling(meta, sets, reps=20):
+    """HBM read ceilings on this GPU from the library's read probe (pkv_read_probe: the decode kernel's loads,
+    wave layout and pipeline, with no arithmetic), over the benchmark's own rotating K/V pools:
+      decode_pattern  the decode's tiles in the decode's order (work-group = (sequence, head) row, entries
+                      block_tables[s, j] * H + h): the decode's gather with the arithmetic removed;
+      random_tiles    every (block, head) tile of the pools once, in a random order, 128 per work-group;
+      sequential      both pools streamed from start to end, 128 tiles per work-group.
+    Each figure is bytes read per launch / mean launch time (HIP events on the launch stream, launches back to
+    back, alternating input sets)."""
+    import torch
+
+    import paged_kv_cache_383_amd as pkv
+    cfg = meta.cfg
+    H, D, bs = cfg.num_heads, cfg.head_dim, cfg.block_size
+    tile = bs * D * elem_bytes(cfg.dtype)
+    dev = sets[0].k_cache.device
+    pool_tiles = meta.num_blocks * H
+    tab = sets[0].block_tables.long()
+    B, M = tab.shape
+    h = torch.arange(H, device=dev, dtype=torch.int64)
+    order_dec = torch.where(tab[:, None, :] >= 0, tab[:, None, :] * H + h[None, :, None],
+                            torch.full_like(tab[:, None, :], -1)).reshape(B * H, M).to(torch.int32).contiguous()
+    n_dec = int((tab >= 0).sum().item()) * H
+    g = torch.Generator(device=dev)
+    g.manual_seed(383383)
+    group = 128
+    n_groups = -(-pool_tiles // group)
+    order_rand = torch.full((n_groups * group,), -1, dtype=torch.int32, device=dev)
+    order_rand[:pool_tiles] = torch.randperm(pool_tiles, generator=g, device=dev).to(torch.int32)
+    sink = torch.empty(8 * max(B * H, n_groups), dtype=torch.int32, device=dev)
+    R = len(sets)
+
+    def timed(order, group_tiles):
+        run = lambda i: pkv.read_probe(sets[i % R].k_cache, sets[i % R].v_cache, tile, order, group_tiles, sink)
+        for i in range(3):
+            run(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            run(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    us_dec = timed(order_dec, M)
+    us_rand = timed(order_rand, group)
+    us_seq = timed(None, group)
+    nbytes = {"decode_pattern": 2 * n_dec * tile, "random_tiles": 2 * pool_tiles * tile,
+              "sequential": 2 * pool_tiles * tile}
+    us = {"decode_pattern": us_dec, "random_tiles": us_rand, "sequential": us_seq}
+    out = {k: {"GB_per_s": round(nbytes[k] / us[k] / 1e3, 1), "mean_launch_us": round(us[k], 2),
+               "bytes_per_launch": nbytes[k]} for k in us}
+    out["tile_bytes"] = tile
+    out["kernel"] = "read_probe_kernel (pkv_read_probe)"
+    return out
 
 
 def parallel_sampling(args):
@@ -488,8 +607,7 @@ def prefill(args):
     tables, ctx = pool.build_tables(list(range(len(lens))), width)
     T = int(lens.sum())
     qs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    slots = np.concatenate([[tables[i][t // bs] * bs + t % bs for t in range(L)]
-                            for i, L in enumerate(lens.tolist())]).astype(np.int64)
+    slots = np.concatenate([pool.slots(i, 0, L) for i, L in enumerate(lens.tolist())])
     gen = torch.Generator(device=dev)
     gen.manual_seed(cfg.seed)
     kc, vc = W.kv_pool(nb, H, bs, D, dt, dev, zero=True)
@@ -590,8 +708,7 @@ def main():
     import paged_kv_cache_383_amd as pkv
     import workloads as W
     from paged_kv_cache_383_amd import build as b
-    if not os.path.exists(b.LIB_PATH):
-        b.build()
+    b.ensure_built()
     pkv.lib()
     if args.workload == "parallel_sampling":
         parallel_sampling(args)
@@ -716,6 +833,9 @@ def main():
 
     stream_ref = torch_stream_reference()
     log(f"plain PyTorch streaming on this GPU: {stream_ref}")
+    probe = read_ceiling(meta, sets)
+    probe["decode_call_over_decode_pattern_time"] = round(probe["decode_pattern"]["mean_launch_us"] / decode_us, 4)
+    log(f"read probe on this GPU: {probe}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -771,7 +891,7 @@ def main():
             "algorithmic_bytes_per_launch": nbytes["decode"],
             "mean_launch_us": round(decode_us, 2),
         },
-        "diagnostic": stream_ref,
+        "diagnostic": {"read_probe": probe, "torch_streaming": stream_ref},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -312,6 +312,14 @@ int pkv_pool_fork(pkv_block_pool* pool, int64_t parent, int64_t child);
 int pkv_pool_append_slots(pkv_block_pool* pool, int64_t seq, int64_t n, int64_t* slots_out,
                           int64_t* copies_out, int64_t max_copies, int64_t* num_copies);
 
+/* Flat slots (block * block_size + offset) of tokens first .. first + n - 1 of
+ * `seq`, which must all be held already (e.g. a prompt just allocated, to be
+ * written with paged_kv_write): slots_out[n] ([explain] Steps 5-6: token t
+ * of a request sits at offset t % block_size of the block its table lists at
+ * t / block_size).  PKV_EINVAL for an unknown sequence or tokens it does not
+ * hold. */
+int pkv_pool_slots(const pkv_block_pool* pool, int64_t seq, int64_t first, int64_t n, int64_t* slots_out);
+
 /* Drop `seq`; blocks no other table holds return to the free list ([explain]
  * Step 7: released blocks are immediately reusable). */
 int pkv_pool_free(pkv_block_pool* pool, int64_t seq);
@@ -346,6 +354,28 @@ typedef struct {
   int64_t shared_blocks;    /* used blocks held by more than one table                    */
 } pkv_pool_usage_t;
 int pkv_pool_usage(const pkv_block_pool* pool, pkv_pool_usage_t* out);
+
+/* The waste comparison derived from pkv_pool_usage ([explain] the step-6
+ * calculation: static reservation of max_model_len slots per request against
+ * the paged blocks).  A zero max_model_len or bytes_per_token leaves the
+ * fields that need it at zero. */
+typedef struct {
+  int64_t empty_slots;      /* allocated_slots - stored_tokens: empty tails of last blocks    */
+  double paged_waste;       /* empty_slots / allocated_slots (0 when nothing is allocated)    */
+  int64_t static_slots;     /* sequences * max_model_len                                      */
+  double static_waste;      /* 1 - logical_tokens / static_slots (0 when static_slots is 0)   */
+  int64_t paged_bytes;      /* allocated_slots * bytes_per_token                              */
+  int64_t stored_bytes;     /* stored_tokens * bytes_per_token                                */
+  int64_t static_bytes;     /* static_slots * bytes_per_token                                 */
+} pkv_waste_t;
+int pkv_pool_waste(const pkv_block_pool* pool, int64_t max_model_len, int64_t bytes_per_token, pkv_waste_t* out);
+
+/* Usage and waste of n requests of the given lengths, each with `samples`
+ * parallel samples sharing its prompt ([explain] Step 9), in a pool of exactly
+ * the blocks the prompts need (request i is allocated as sequence i * samples
+ * and forked samples - 1 times). */
+int pkv_account(const int64_t* lens, int32_t n, int32_t block_size, int32_t samples, int64_t max_model_len,
+                int64_t bytes_per_token, pkv_pool_usage_t* usage_out, pkv_waste_t* waste_out);
 
 /*
  * ---- Batch: decode rows over a pool, with a mirror of the device tables ----

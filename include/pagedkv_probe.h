@@ -1,0 +1,60 @@
+/*
+ * pagedkv_probe.h -- diagnostic entry point of libpagedkv.so: an HBM read
+ * ceiling for the decode kernel's access pattern.
+ *
+ * Decode reads the whole K/V cache once per step and is bound by memory
+ * bandwidth ("vLLM KV cache and PagedAttention explained", Step 6: every
+ * decode step reads the entire KV cache).  Its fraction of the 8 TB/s HBM
+ * peak is one yardstick; this probe gives another, measured on the same GPU:
+ * how fast the same kind of loads, with no arithmetic at all, can stream the
+ * same kind of tiles.  It is not part of the decode path.
+ *
+ * Same conventions as pagedkv.h: device pointers owned by the caller, the
+ * call is asynchronous on `stream` (a hipStream_t passed as void*), host-side
+ * validation first, a non-zero pkv_status (see pagedkv.h) with nothing
+ * launched on failure, text in pkv_last_error().
+ */
+#ifndef PAGEDKV_PROBE_H
+#define PAGEDKV_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * pkv_read_probe -- read tiles of tile_bytes bytes (4096 or 8192) from pool a
+ * and, when b is not NULL, the tile at the same index of pool b as well (the
+ * decode kernel reads a block's K and V tiles together).
+ *
+ *   a, b          device pools of pool_tiles tiles each, 16-byte aligned
+ *   order         int32 [num_groups * group_tiles]: the tile indices to read,
+ *                 or NULL for 0, 1, 2, ... (a sequential stream of num_groups *
+ *                 group_tiles tiles).  An entry outside [0, pool_tiles) is
+ *                 skipped without a memory access (use -1 to pad).
+ *   num_groups    work-groups; group g reads entries g*group_tiles ..
+ *                 (g+1)*group_tiles - 1 of the order
+ *   group_tiles   entries per work-group (>= 1)
+ *   sink          uint32 [num_groups * 8], written: one XOR of the data per
+ *                 wave, so that no load can be dropped
+ *
+ * Work decomposition, as in the decode kernel: 8 wave64 per work-group; a
+ * wave works in stages of 8 KiB per pool (two 4 KiB tiles or one 8 KiB tile),
+ * wave w taking stages w, w + 8, ... of its group; 16-byte non-temporal
+ * buffer loads per lane, two stages of both pools in flight per wave.  With
+ * the decode's own tile order (group = (sequence, head) row, entries =
+ * block_tables[s, j] * num_heads + h, padded with -1) this is the decode's
+ * gather with the arithmetic removed; with a random permutation it is a
+ * random-tile read; with order NULL a sequential stream.
+ * Bytes read per call = (1 or 2 pools) * tile_bytes * number of valid entries.
+ */
+int pkv_read_probe(const void* a, const void* b, int64_t pool_tiles, int32_t tile_bytes, const int32_t* order,
+                   int32_t num_groups, int32_t group_tiles, uint32_t* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_PROBE_H */

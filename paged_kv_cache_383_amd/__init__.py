@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
             "pkv_pool_num_tokens": ([vp, i64], i64), "pkv_pool_table": ([vp, i64, vp, i64], i64),
             "pkv_pool_free_list": ([vp, vp, i64], i64),
             "pkv_pool_usage": ([vp, vp], ctypes.c_int),
+            "pkv_pool_slots": ([vp, i64, i64, i64, vp], ctypes.c_int),
+            "pkv_pool_waste": ([vp, i64, i64, vp], ctypes.c_int),
+            "pkv_account": ([vp, i32, i32, i32, i64, i64, vp, vp], ctypes.c_int),
             "paged_attention_decode_step": ([vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i64,
                                              ctypes.c_float, i32, vp, vp, sz, i32, vp], ctypes.c_int),
             "paged_attention_prefill": ([vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i64,
@@ -88,6 +91,7 @@ def lib() -> ctypes.CDLL:
             "pkv_batch_set_row": ([vp, i32, i64], ctypes.c_int),
             "pkv_batch_plan_step": ([vp, i32, vp, i64, vp, vp, vp, i64, vp], ctypes.c_int),
             "paged_kv_prepare_step": ([vp, i32, vp, i32, vp, i64, vp, vp, i32, i64, vp], ctypes.c_int),
+            "pkv_read_probe": ([vp, vp, i64, i32, vp, i32, i32, vp, vp], ctypes.c_int),
         }
         for name, (args, res) in pool_fns.items():
             getattr(L, name).argtypes = args
@@ -253,6 +257,35 @@ def paged_attention_decode_step(q, k_new, v_new, k_cache, v_cache, block_tables,
     return out
 
 
+def read_probe(a, b, tile_bytes: int, order, group_tiles: int, sink, num_groups=None):
+    """Diagnostic HBM read (include/pagedkv_probe.h): tiles of ``tile_bytes`` of pools ``a`` and ``b`` (b may be
+    None) in the order of the int32 tensor ``order`` (None: sequential), ``group_tiles`` entries per work-group;
+    ``sink`` int32 receives one word per wave."""
+    import torch
+    _device_tensor("a", a)
+    if b is not None:
+        _device_tensor("b", b, a.dtype)
+        if b.numel() != a.numel():
+            raise ValueError("pools a and b must have the same size")
+    pool_bytes = a.numel() * a.element_size()
+    pool_tiles = pool_bytes // int(tile_bytes)
+    if order is not None:
+        _device_tensor("order", order, torch.int32)
+        n = order.numel()
+        if n % int(group_tiles):
+            raise ValueError("order must hold whole groups")
+        groups = n // int(group_tiles)
+    else:
+        groups = num_groups if num_groups is not None else -(-pool_tiles // int(group_tiles))
+    _device_tensor("sink", sink, torch.int32)
+    if sink.numel() < 8 * groups:
+        raise ValueError("sink needs 8 words per work-group")
+    _check(_launch(a.device, lib().pkv_read_probe, a.data_ptr(), None if b is None else b.data_ptr(), pool_tiles,
+                   int(tile_bytes), None if order is None else order.data_ptr(), int(groups), int(group_tiles),
+                   sink.data_ptr()))
+    return groups
+
+
 def paged_attention_prefill(q, k_cache, v_cache, block_tables, query_start, context_lens, scale,
                             max_query_len: int, out=None):
     """Causal attention of packed new tokens q [T, H, D] over their sequences' paged caches; sequence i owns
@@ -293,6 +326,33 @@ def paged_kv_copy_blocks(k_cache, v_cache, block_mapping):
     NB, H, bs, D = k_cache.shape
     _check(_launch(k_cache.device, lib().paged_kv_copy_blocks, k_cache.data_ptr(), v_cache.data_ptr(),
                    block_mapping.data_ptr(), block_mapping.shape[0], NB, H, D, bs, _dtype_code(k_cache)))
+
+
+class _Usage(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("num_blocks", "free_blocks", "used_blocks", "sequences",
+                                              "logical_tokens", "stored_tokens", "allocated_slots",
+                                              "shared_blocks")]
+
+
+class _Waste(ctypes.Structure):
+    _fields_ = [("empty_slots", ctypes.c_int64), ("paged_waste", ctypes.c_double), ("static_slots", ctypes.c_int64),
+                ("static_waste", ctypes.c_double), ("paged_bytes", ctypes.c_int64), ("stored_bytes", ctypes.c_int64),
+                ("static_bytes", ctypes.c_int64)]
+
+
+def _fields(st) -> dict:
+    return {name: getattr(st, name) for name, _ in st._fields_}
+
+
+def account(lens, block_size: int = 16, max_model_len: int = 0, bytes_per_token: int = 0, samples: int = 1):
+    """(usage, waste) dicts of requests of the given lengths, each with ``samples`` parallel samples sharing its
+    prompt, in a pool of exactly the blocks the prompts need (pkv_account)."""
+    import numpy as np
+    L = np.ascontiguousarray(np.asarray(lens, dtype=np.int64))
+    u, w = _Usage(), _Waste()
+    _check(lib().pkv_account(L.ctypes.data if len(L) else None, len(L), int(block_size), int(samples),
+                             int(max_model_len), int(bytes_per_token), ctypes.byref(u), ctypes.byref(w)))
+    return _fields(u), _fields(w)
 
 
 class BlockPool:
@@ -336,6 +396,13 @@ class BlockPool:
                                            ctypes.byref(k)))
         return slots[:int(n)], copies[:k.value]
 
+    def slots(self, seq: int, first: int, n: int):
+        """int64 [n]: flat slots of tokens first .. first + n - 1 that ``seq`` already holds."""
+        import numpy as np
+        out = np.empty(max(int(n), 1), dtype=np.int64)
+        _check(lib().pkv_pool_slots(self._h, int(seq), int(first), int(n), out.ctypes.data))
+        return out[:int(n)]
+
     def free_sequence(self, seq: int):
         _check(lib().pkv_pool_free(self._h, int(seq)))
 
@@ -362,12 +429,15 @@ class BlockPool:
 
     def usage(self) -> dict:
         """Slot accounting: blocks used / free, stored vs logical tokens, allocated slots, shared blocks."""
-        import numpy as np
-        names = ("num_blocks", "free_blocks", "used_blocks", "sequences", "logical_tokens", "stored_tokens",
-                 "allocated_slots", "shared_blocks")
-        buf = np.zeros(len(names), dtype=np.int64)
-        _check(lib().pkv_pool_usage(self._h, buf.ctypes.data))
-        return dict(zip(names, (int(x) for x in buf)))
+        u = _Usage()
+        _check(lib().pkv_pool_usage(self._h, ctypes.byref(u)))
+        return _fields(u)
+
+    def waste(self, max_model_len: int = 0, bytes_per_token: int = 0) -> dict:
+        """Paged vs static-reservation waste of the pool's current contents (pkv_pool_waste)."""
+        w = _Waste()
+        _check(lib().pkv_pool_waste(self._h, int(max_model_len), int(bytes_per_token), ctypes.byref(w)))
+        return _fields(w)
 
     def free_list(self):
         import numpy as np

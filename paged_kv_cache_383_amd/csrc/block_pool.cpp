@@ -155,6 +155,22 @@ extern "C" int pkv_pool_append_slots(pkv_block_pool* p, int64_t seq, int64_t n, 
   return pkv::set_error(PKV_OK, "");
 }
 
+extern "C" int pkv_pool_slots(const pkv_block_pool* p, int64_t seq, int64_t first, int64_t n, int64_t* slots_out) {
+  if (!p || n < 0 || first < 0 || (n > 0 && !slots_out))
+    return pool_fail(PKV_EINVAL, "null pool or output, or negative position or count");
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return pool_fail(PKV_EINVAL, "unknown sequence " + std::to_string(seq));
+  const Sequence& s = it->second;
+  if (first + n > s.tokens)
+    return pool_fail(PKV_EINVAL, "tokens [" + std::to_string(first) + ", " + std::to_string(first + n) +
+                                     ") are not all held by sequence " + std::to_string(seq) + " (" +
+                                     std::to_string(s.tokens) + " tokens)");
+  const int64_t bs = p->block_size;
+  for (int64_t t = first; t < first + n; ++t)
+    slots_out[t - first] = int64_t(s.table[size_t(t / bs)]) * bs + t % bs;
+  return pkv::set_error(PKV_OK, "");
+}
+
 extern "C" int pkv_pool_free(pkv_block_pool* p, int64_t seq) {
   if (!p) return pool_fail(PKV_EINVAL, "null pool");
   auto it = p->seqs.find(seq);
@@ -225,6 +241,50 @@ extern "C" int pkv_pool_usage(const pkv_block_pool* p, pkv_pool_usage_t* out) {
   u.allocated_slots = u.used_blocks * bs;
   *out = u;
   return pkv::set_error(PKV_OK, "");
+}
+
+extern "C" int pkv_pool_waste(const pkv_block_pool* p, int64_t max_model_len, int64_t bytes_per_token,
+                              pkv_waste_t* out) {
+  if (!p || !out || max_model_len < 0 || bytes_per_token < 0)
+    return pool_fail(PKV_EINVAL, "null pool or output, or negative max_model_len / bytes_per_token");
+  pkv_pool_usage_t u{};
+  if (int rc = pkv_pool_usage(p, &u)) return rc;
+  pkv_waste_t w{};
+  w.empty_slots = u.allocated_slots - u.stored_tokens;
+  w.paged_waste = u.allocated_slots ? double(w.empty_slots) / double(u.allocated_slots) : 0.0;
+  w.static_slots = u.sequences * max_model_len;
+  w.static_waste = w.static_slots ? 1.0 - double(u.logical_tokens) / double(w.static_slots) : 0.0;
+  w.paged_bytes = u.allocated_slots * bytes_per_token;
+  w.stored_bytes = u.stored_tokens * bytes_per_token;
+  w.static_bytes = w.static_slots * bytes_per_token;
+  *out = w;
+  return pkv::set_error(PKV_OK, "");
+}
+
+extern "C" int pkv_account(const int64_t* lens, int32_t n, int32_t block_size, int32_t samples,
+                           int64_t max_model_len, int64_t bytes_per_token, pkv_pool_usage_t* usage_out,
+                           pkv_waste_t* waste_out) {
+  if (n < 0 || (n > 0 && !lens) || block_size <= 0 || samples < 1 || !usage_out || !waste_out)
+    return pool_fail(PKV_EINVAL, "bad lengths, block_size, samples or null output");
+  int64_t need = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (lens[i] < 0) return pool_fail(PKV_EINVAL, "negative request length");
+    need += (lens[i] + block_size - 1) / block_size;
+  }
+  if (need > INT32_MAX) return pool_fail(PKV_EINVAL, "too many blocks");
+  // Exactly the blocks the prompts need: forks share them and allocate nothing.
+  pkv_block_pool* p = pkv_pool_create(std::max<int64_t>(need, 1), block_size, nullptr);
+  if (!p) return pool_fail(PKV_EINVAL, "out of host memory");
+  int rc = PKV_OK;
+  for (int32_t i = 0; i < n && rc == PKV_OK; ++i) {
+    rc = pkv_pool_allocate(p, int64_t(i) * samples, lens[i]);
+    for (int32_t s = 1; s < samples && rc == PKV_OK; ++s)
+      rc = pkv_pool_fork(p, int64_t(i) * samples, int64_t(i) * samples + s);
+  }
+  if (rc == PKV_OK) rc = pkv_pool_usage(p, usage_out);
+  if (rc == PKV_OK) rc = pkv_pool_waste(p, max_model_len, bytes_per_token, waste_out);
+  pkv_pool_destroy(p);
+  return rc;
 }
 
 extern "C" int pkv_pool_build_tables(const pkv_block_pool* p, const int64_t* seqs, int32_t n, int32_t width,
@@ -318,7 +378,12 @@ extern "C" int pkv_batch_plan_step(pkv_batch* b, int32_t tokens_per_row, int32_t
   // Check first, so that a failure changes nothing: every active row's
   // sequence exists, stays within the table width, and the free list covers
   // the step's new blocks and copies.
+  // A shared, partly filled last block X with reference count c that k rows
+  // of the step append into is copied min(k, c - 1) times: each writer but
+  // the last holder takes a private copy (pkv_pool_append_slots), and every
+  // copy lowers X's count by one.
   int64_t need = 0, copies = 0;
+  std::unordered_map<int32_t, int64_t> writers;        // shared last block -> rows appending into it
   for (int32_t r = 0; r < b->rows; ++r) {
     const int64_t s = b->seq[size_t(r)];
     if (s < 0) continue;
@@ -330,11 +395,11 @@ extern "C" int pkv_batch_plan_step(pkv_batch* b, int32_t tokens_per_row, int32_t
     if (nb > b->width)
       return pool_fail(PKV_EINVAL, "sequence " + std::to_string(s) + " would outgrow the batch tables");
     need += nb - int64_t(q.table.size());
-    if (tokens_per_row > 0 && q.tokens % bs != 0 && p->refcount[size_t(q.table.back())] > 1) {
-      ++need;
-      ++copies;
-    }
+    if (tokens_per_row > 0 && q.tokens % bs != 0 && p->refcount[size_t(q.table.back())] > 1)
+      ++writers[q.table.back()];
   }
+  for (const auto& w : writers) copies += std::min<int64_t>(w.second, p->refcount[size_t(w.first)] - 1);
+  need += copies;
   if (copies > max_copies) return pool_fail(PKV_EINVAL, "room for " + std::to_string(copies) + " copies is needed");
   if (need > int64_t(p->free_list.size()))
     return pool_fail(PKV_ENOSPACE, std::to_string(need) + " blocks needed, " +

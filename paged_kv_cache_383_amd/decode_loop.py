@@ -65,11 +65,8 @@ class DecodeLoop:
         (device [P, H, D]); the prompt is written at the next step, before its decode."""
         assert self.row_seq[row] < 0, "row is busy"
         P = int(k_prompt.shape[0])
-        table = self.pool.allocate(seq, P)
-        bs = self.block_size
-        t = np.asarray(table, dtype=np.int64)
-        pos = np.arange(P, dtype=np.int64)
-        self._pending.append((t[pos // bs] * bs + pos % bs, k_prompt, v_prompt))
+        self.pool.allocate(seq, P)
+        self._pending.append((self.pool.slots(seq, 0, P), k_prompt, v_prompt))
         self.batch.set_row(row, seq)
         self.row_seq[row] = seq
 

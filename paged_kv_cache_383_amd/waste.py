@@ -4,8 +4,9 @@ Reproduces the comparison of "vLLM KV cache and PagedAttention explained"
 (hrletsgo.me), the Korean step-6 calculation and "Why Waste Stays Below 4%":
 static reservation gives every request max_model_len contiguous slots, while
 PagedAttention gives it ceil(n / block_size) blocks, so only the tail of each
-request's last block is empty.  The counting is the library's block pool
-(pkv_pool_usage); this script only feeds it lengths and formats the result.
+request's last block is empty.  The counting and the waste fractions are the library's
+(pkv_account, over its block pool); this script only feeds it lengths and
+formats the result.
 
     python -m paged_kv_cache_383_amd.waste 6 50 8 100 --block-size 16 \\
         --max-model-len 2048 --bytes-per-token 819200
@@ -17,29 +18,22 @@ import json
 
 
 def account(lens, block_size=16, max_model_len=None, bytes_per_token=None, samples=1):
-    """Slot accounting for requests of the given lengths (each with ``samples`` parallel samples sharing
-    its prompt, [explain] Step 9).  Returns the pool's usage plus the derived waste fractions."""
-    from . import BlockPool
-    need = sum(-(-int(L) // block_size) for L in lens) * max(1, samples)
-    pool = BlockPool(max(need, 1), block_size)
-    for i, L in enumerate(lens):
-        pool.allocate(i * samples, int(L))
-        for s in range(1, samples):
-            pool.fork(i * samples, i * samples + s)
-    u = pool.usage()
-    r = dict(u)
-    r["empty_slots"] = u["allocated_slots"] - u["stored_tokens"]
-    r["paged_waste"] = r["empty_slots"] / u["allocated_slots"] if u["allocated_slots"] else 0.0
+    """Slot accounting for requests of the given lengths (each with ``samples`` parallel samples sharing its
+    prompt, [explain] Step 9): the pool's usage and the waste comparison, both computed by the library
+    (pkv_account); only the fields that were asked for are reported."""
+    from . import account as lib_account
+    usage, waste = lib_account(lens, block_size, max_model_len or 0, bytes_per_token or 0, max(1, samples))
+    r = dict(usage)
+    r["empty_slots"] = waste["empty_slots"]
+    r["paged_waste"] = waste["paged_waste"]
     if max_model_len:
-        reserved = u["sequences"] * int(max_model_len)
-        r["static_slots"] = reserved
-        r["static_waste"] = 1.0 - u["logical_tokens"] / reserved
+        r["static_slots"] = waste["static_slots"]
+        r["static_waste"] = waste["static_waste"]
     if bytes_per_token:
-        b = int(bytes_per_token)
-        r["paged_bytes"] = u["allocated_slots"] * b
-        r["stored_bytes"] = u["stored_tokens"] * b
+        r["paged_bytes"] = waste["paged_bytes"]
+        r["stored_bytes"] = waste["stored_bytes"]
         if max_model_len:
-            r["static_bytes"] = r["static_slots"] * b
+            r["static_bytes"] = waste["static_bytes"]
     return r
 
 

@@ -21,8 +21,7 @@ import oracle_pins as P
 def pkv():
     from paged_kv_cache_383_amd import build as b
     import os
-    if not os.path.exists(b.LIB_PATH):
-        b.build()
+    b.ensure_built()
     import paged_kv_cache_383_amd as m
     m.lib()
     return m
@@ -192,3 +191,154 @@ def test_waste_tool_reproduces_the_pages_example(pkv):
     assert r["static_bytes"] == 8192 * 819200 and r["paged_bytes"] == 208 * 819200
     s = account([100], 16, samples=4)          # parallel samples: the prompt's blocks are stored once
     assert s["stored_tokens"] == 100 and s["logical_tokens"] == 400 and s["shared_blocks"] == 7
+
+
+def test_pool_waste_matches_oracle_accounting(pkv):
+    """pkv_pool_waste against the oracle's usage and waste fractions, over random pools with sharing."""
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        NB, bs = int(rng.integers(8, 60)), int(rng.choice([16, 32]))
+        ref, lib = BM.BlockPool(NB, bs), pkv.BlockPool(NB, bs)
+        live, nxt = [], 0
+        for _ in range(30):
+            r = rng.random()
+            try:
+                if r < 0.4 or not live:
+                    n = int(rng.integers(0, 3 * bs))
+                    ref.allocate(nxt, n)
+                    lib.allocate(nxt, n)
+                    live.append(nxt)
+                    nxt += 1
+                elif r < 0.6:
+                    ref.fork(live[0], nxt)
+                    lib.fork(live[0], nxt)
+                    live.append(nxt)
+                    nxt += 1
+                else:
+                    s = live[int(rng.integers(len(live)))]
+                    n = int(rng.integers(0, bs))
+                    ref.append_slots(s, n)
+                    lib.append_slots(s, n)
+            except (BM.OutOfBlocks, pkv.OutOfBlocks):
+                break
+        u = BM.usage(ref)
+        M = int(rng.integers(1, 4096))
+        w = lib.waste(M, 819200)
+        assert w["empty_slots"] == u["allocated_slots"] - u["stored_tokens"]
+        assert abs(w["paged_waste"] - BM.paged_waste(u)) < 1e-12
+        assert abs(w["static_waste"] - BM.static_waste(u, M)) < 1e-12
+        assert w["static_slots"] == u["sequences"] * M
+        assert (w["paged_bytes"], w["stored_bytes"], w["static_bytes"]) == (
+            u["allocated_slots"] * 819200, u["stored_tokens"] * 819200, u["sequences"] * M * 819200)
+
+
+def test_account_matches_oracle_pool(pkv):
+    """pkv_account (requests + parallel samples in an exactly sized pool) against the oracle pool."""
+    rng = np.random.default_rng(11)
+    for trial in range(30):
+        bs = int(rng.choice([16, 32]))
+        lens = rng.integers(0, 300, int(rng.integers(1, 8))).tolist()
+        samples = int(rng.integers(1, 5))
+        need = sum(-(-L // bs) for L in lens)
+        ref = BM.BlockPool(max(need, 1), bs)
+        for i, L in enumerate(lens):
+            ref.allocate(i * samples, L)
+            for s in range(1, samples):
+                ref.fork(i * samples, i * samples + s)
+        usage, waste = pkv.account(lens, bs, 2048, 0, samples)
+        assert usage == BM.usage(ref)
+        assert abs(waste["paged_waste"] - BM.paged_waste(usage)) < 1e-12
+        assert abs(waste["static_waste"] - BM.static_waste(usage, 2048)) < 1e-12
+
+
+def test_pool_slots_are_where_the_gather_reads(pkv):
+    """Slots from pkv_pool_slots, written with the oracle's kv_write, are read back by the oracle's gather
+    through the same table in token order (the slot of token t is block table[t // bs], offset t % bs)."""
+    rng = np.random.default_rng(5)
+    for bs in (16, 32):
+        NB, H, D = 40, 2, 8
+        p = pkv.BlockPool(NB, bs, rng.permutation(NB))
+        lens = [1, bs - 1, bs, bs + 1, 3 * bs + 5]
+        kc = np.full((NB, H, bs, D), np.nan, dtype=np.float32)
+        vc = np.full_like(kc, np.nan)
+        for i, L in enumerate(lens):
+            p.allocate(i, L)
+            k = rng.standard_normal((L, H, D)).astype(np.float32)
+            slots = p.slots(i, 0, L)
+            kc, vc = O.kv_write(k, -k, slots, kc, vc, bs)
+            got = O.gather_sequence(kc, p.table(i), L, bs, "f32")          # [H, L, D]
+            assert np.array_equal(got, k.transpose(1, 0, 2).astype(np.float64))
+            part = p.slots(i, L // 2, L - L // 2)
+            assert np.array_equal(part, slots[L // 2:])
+        with pytest.raises(pkv.PagedKVError, match="not all held"):
+            p.slots(0, 0, 2)
+        with pytest.raises(pkv.PagedKVError, match="unknown sequence"):
+            p.slots(99, 0, 1)
+
+
+def _plan_vs_oracle(pkv, NB, bs, build, rows):
+    """Drive a Batch over the C++ pool and the oracle pool the same way; one decode step (one token per row)
+    must succeed in the batch exactly when the oracle's row-by-row appends succeed, with the same tables."""
+    import copy
+    ref = BM.BlockPool(NB, bs)
+    lib = pkv.BlockPool(NB, bs)
+    build(ref)
+    build(lib)
+    batch = pkv.Batch(lib, len(rows), 64)
+    for r, s in enumerate(rows):
+        batch.set_row(r, s)
+    trial = copy.deepcopy(ref)
+    try:
+        for s in rows:
+            trial.append_slots(s, 1)
+        ok = True
+    except BM.OutOfBlocks:
+        ok = False
+    before = [lib.table(s) for s in rows]
+    if ok:
+        _, lens, copies = batch.plan_step(1)
+        assert [lib.table(s) for s in rows] == [trial.table(s) for s in rows]
+        assert lens.tolist() == [trial.tokens[s] for s in rows]
+        assert lib.free_list() == trial.free
+    else:
+        with pytest.raises(pkv.OutOfBlocks):
+            batch.plan_step(1)
+        assert [lib.table(s) for s in rows] == before
+    return ok
+
+
+def test_plan_step_counts_copies_like_row_by_row_appends(pkv):
+    """Forked sequences that share a partly filled last block, all in one batch: each writer but the last
+    holder copies the block, so the step needs min(k, refcount - 1) copies, not one per writer.  With a free
+    list of exactly that many blocks the step must go through (one short: refused, nothing changed)."""
+    def shared(ref):                     # seq 1: 20 tokens (blocks 0, 1), forked to seq 2
+        ref.allocate(1, 20)
+        ref.fork(1, 2)
+    assert _plan_vs_oracle(pkv, 3, 16, shared, [1, 2])           # 1 copy, 1 free block
+    assert not _plan_vs_oracle(pkv, 2, 16, shared, [1, 2])
+
+    def three(ref):                      # three holders, two of them in the batch: both writers copy
+        ref.allocate(1, 20)
+        ref.fork(1, 2)
+        ref.fork(1, 3)
+    assert _plan_vs_oracle(pkv, 4, 16, three, [1, 2])
+    assert not _plan_vs_oracle(pkv, 3, 16, three, [1, 2])
+    assert _plan_vs_oracle(pkv, 4, 16, three, [1, 2, 3])         # 2 copies, the last holder in place
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        bs = 16
+
+        def build(ref, seed=trial):
+            g = np.random.default_rng(seed)
+            ref.allocate(0, int(g.integers(1, 60)))
+            for s in range(1, int(g.integers(2, 6))):
+                ref.fork(int(g.integers(0, s)), s)
+                if g.random() < 0.5:
+                    ref.append_slots(s, int(g.integers(0, 20)))
+        probe = BM.BlockPool(200, bs)
+        build(probe)
+        seqs = sorted(probe.tables)
+        rows = [s for s in seqs if rng.random() < 0.7] or seqs[:1]
+        used = 200 - probe.num_free()
+        extra = int(rng.integers(0, 4))
+        _plan_vs_oracle(pkv, used + extra, bs, build, rows)
