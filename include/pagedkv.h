@@ -31,7 +31,8 @@
  *
  * Pointers and ownership.  Every array argument is a DEVICE pointer to memory
  * the caller allocated and owns; the library allocates nothing, keeps no state
- * between calls and never retains a pointer.  `stream` is a hipStream_t passed
+ * between calls and never retains a pointer (the one exception is the scratch
+ * array of paged_attention_decode_step_noalloc, below).  `stream` is a hipStream_t passed
  * as void* (NULL = the legacy default stream).  All work is enqueued
  * asynchronously on `stream`; nothing synchronises with the host except in
  * PKV_DEBUG mode (below).  Outputs must not alias inputs.  Arrays of
@@ -264,6 +265,30 @@ int paged_attention_decode_step(const void* q, const void* k_new, const void* v_
                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                 int32_t block_size, int64_t num_blocks, float scale, int32_t dtype, void* out,
                                 void* workspace, size_t workspace_bytes, int32_t partition_size, void* stream);
+
+/*
+ * paged_attention_decode_step_noalloc -- paged_attention_decode_step for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments and
+ * results, without the workspace: the split-context partials go to a scratch
+ * array of PKV_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds on each
+ * GPU it runs on, until the process ends.  The call allocates nothing (no
+ * hipMalloc, no allocating library routine); its first call on a device looks
+ * up that device's copy of the array.
+ *
+ * Returns PKV_EWORKSPACE, with nothing launched, when the split would need
+ * more scratch than that (paged_attention_workspace_bytes for the same sizes
+ * and partition_size above 16 MiB): choose a larger partition_size, or call
+ * paged_attention_decode_step with a workspace.  Every call on one GPU uses
+ * that GPU's one array, so calls that overlap on one GPU (other streams, other
+ * host threads) race with each other; the caller must order them.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int paged_attention_decode_step_noalloc(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                        void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                        int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                        int32_t dtype, void* out, int32_t partition_size, void* stream);
 
 /* Text of the calling thread's last non-OK status (empty string if none). */
 const char* pkv_last_error(void);

@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
             "pkv_batch_plan_step": ([vp, i32, vp, i64, vp, vp, vp, i64, vp], ctypes.c_int),
             "paged_kv_prepare_step": ([vp, i32, vp, i32, vp, i64, vp, vp, i32, i64, vp], ctypes.c_int),
             "pkv_read_probe": ([vp, vp, i64, i32, vp, i32, i32, vp, vp], ctypes.c_int),
+            "paged_attention_decode_step_noalloc": ([vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i64,
+                                                     ctypes.c_float, i32, vp, i32, vp], ctypes.c_int),
         }
         for name, (args, res) in pool_fns.items():
             getattr(L, name).argtypes = args
@@ -255,6 +257,37 @@ def paged_attention_decode_step(q, k_new, v_new, k_cache, v_cache, block_tables,
                    H, D, bs, NB, float(scale), _dtype_code(q), out.data_ptr(), workspace.data_ptr(), ws_bytes,
                    partition_size))
     return out
+
+
+def paged_attention_decode_step_noalloc(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                                        out, partition_size=DEFAULT_PARTITION):
+    """paged_attention_decode_step without a workspace, for callers that cannot allocate: the library keeps
+    the split-context partials in its own per-GPU scratch array (calls that overlap on one GPU race).
+    ``out`` must be given, so that the call allocates nothing."""
+    import torch
+    _device_tensor("q", q, k_cache.dtype, 3)
+    _device_tensor("k_new", k_new, k_cache.dtype, 3)
+    _device_tensor("v_new", v_new, k_cache.dtype, 3)
+    _device_tensor("k_cache", k_cache, None, 4)
+    _device_tensor("v_cache", v_cache, k_cache.dtype, 4)
+    _device_tensor("block_tables", block_tables, torch.int32, 2)
+    _device_tensor("context_lens", context_lens, torch.int32, 1)
+    _device_tensor("out", out, q.dtype, 3)
+    NB, H, bs, D = k_cache.shape
+    B = q.shape[0]
+    if (v_cache.shape != k_cache.shape or q.shape[1:] != (H, D) or k_new.shape != q.shape or v_new.shape != q.shape
+            or out.shape != q.shape):
+        raise ValueError("q, k_new, v_new, out [B, H, D] and caches [NB, H, bs, D] do not match")
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    _check(_launch(q.device, lib().paged_attention_decode_step_noalloc, q.data_ptr(), k_new.data_ptr(),
+                   v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                   block_tables.shape[1], context_lens.data_ptr(), B, H, D, bs, NB, float(scale), _dtype_code(q),
+                   out.data_ptr(), partition_size))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def read_probe(a, b, tile_bytes: int, order, group_tiles: int, sink, num_groups=None):

@@ -29,7 +29,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libpagedkv.so")
 STAMP_PATH = LIB_PATH + ".sha256"
-SOURCES = ["api.hip", "kv_write.hip", "decode.hip", "copy_blocks.hip", "step.hip",
+SOURCES = ["api.hip", "kv_write.hip", "decode.hip", "decode_noalloc.hip", "copy_blocks.hip", "step.hip",
            "prefill.hip", "read_probe.hip", "block_pool.cpp"]
 ARCH = "gfx950"
 # The host pass's notice about the device-only feature above; nothing else is filtered.

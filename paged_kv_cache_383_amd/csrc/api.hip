@@ -296,11 +296,13 @@ namespace {
 
 // Decode, optionally with the newest tokens' K/V appended first (k_new, v_new
 // non-null: the fused step).
+// With static_scratch the split-context partials go to the library's own
+// per-device array (pkv::static_scratch) instead of a caller workspace.
 int decode_common(const void* q, const void* k_new, const void* v_new, const void* k_cache, const void* v_cache,
                   const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                   int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                   float scale, int32_t dtype, void* out, void* workspace, size_t workspace_bytes,
-                  int32_t partition_size, void* stream) {
+                  int32_t partition_size, void* stream, bool static_scratch = false) {
   if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs must be >= 0 (got %d)", num_seqs);
   if (int rc = check_shape(dtype, num_heads, head_dim, block_size, num_blocks)) return rc;
   if (max_blocks_per_seq <= 0)
@@ -327,7 +329,11 @@ int decode_common(const void* q, const void* k_new, const void* v_new, const voi
   const int64_t parts = partitions_for(max_blocks_per_seq, pb);
   if (parts > 65535) return fail(PKV_EUNSUPPORTED, "%lld partitions exceed the grid limit 65535", (long long)parts);
   const pkv::WorkspaceLayout wl = pkv::workspace_layout(num_seqs, num_heads, head_dim, parts);
-  if (wl.bytes > 0 && (workspace == nullptr || workspace_bytes < wl.bytes))
+  if (static_scratch && wl.bytes > pkv::kStaticScratchBytes)
+    return fail(PKV_EWORKSPACE, "the split needs %zu bytes of scratch, more than the %zu bytes the no-allocation "
+                "entry point holds per GPU; use a larger partition_size or paged_attention_decode_step with a "
+                "workspace", wl.bytes, pkv::kStaticScratchBytes);
+  if (!static_scratch && wl.bytes > 0 && (workspace == nullptr || workspace_bytes < wl.bytes))
     return fail(PKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given%s", wl.bytes, workspace_bytes,
                 workspace ? "" : " (null)");
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -349,6 +355,10 @@ int decode_common(const void* q, const void* k_new, const void* v_new, const voi
                       (long long)num_blocks);
       }
     }
+  }
+  if (static_scratch && wl.bytes > 0) {            // after validation: the first call on a device sets up
+    hipError_t e = pkv::static_scratch(&workspace);
+    if (e != hipSuccess) return hip_fail(e, "scratch address of the no-allocation entry point");
   }
   pkv::DecodeArgs a{};
   a.q = q;
@@ -398,4 +408,16 @@ extern "C" int paged_attention_decode_step(const void* q, const void* k_new, con
   return decode_common(q, k_new, v_new, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                        num_seqs, num_heads, head_dim, block_size, num_blocks, scale, dtype, out, workspace,
                        workspace_bytes, partition_size, stream);
+}
+
+extern "C" int paged_attention_decode_step_noalloc(const void* q, const void* k_new, const void* v_new,
+                                                   void* k_cache, void* v_cache, const int32_t* block_tables,
+                                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                                   int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                                   int32_t block_size, int64_t num_blocks, float scale,
+                                                   int32_t dtype, void* out, int32_t partition_size, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return fail(PKV_EINVAL, "null k_new or v_new");
+  return decode_common(q, k_new, v_new, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_heads, head_dim, block_size, num_blocks, scale, dtype, out, nullptr, 0,
+                       partition_size, stream, true);
 }

@@ -61,6 +61,13 @@ struct DecodeArgs {
 hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodeArgs& a,
                          hipStream_t stream);
 
+// Split-context scratch of paged_attention_decode_step_noalloc: a device array
+// of kStaticScratchBytes that the library holds on every GPU it runs on.
+// static_scratch() returns the current device's copy (looked up once per
+// device, with that device current; decode_noalloc.hip).
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+hipError_t static_scratch(void** ptr);
+
 hipError_t launch_kv_write(int dtype, int head_dim, const void* k, const void* v,
                            const int64_t* slot_mapping, int64_t num_tokens, void* k_cache,
                            void* v_cache, int64_t num_blocks, int32_t num_heads,
