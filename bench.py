@@ -277,15 +277,17 @@ def torch_stream_reference(reps=20):
             "note": "plain PyTorch streaming on the same GPU (torch.neg copy, torch.sum read), events"}
 
 
-def read_ceiling(meta, sets, reps=20):
-    """HBM read ceilings on this GPU from the library's read probe (pkv_read_probe: the decode kernel's loads,
-    wave layout and pipeline, with no arithmetic), over the benchmark's own rotating K/V pools:
-      decode_pattern  the decode's tiles in the decode's order (work-group = (sequence, head) row, entries
-                      block_tables[s, j] * H + h): the decode's gather with the arithmetic removed;
-      random_tiles    every (block, head) tile of the pools once, in a random order, 128 per work-group;
-      sequential      both pools streamed from start to end, 128 tiles per work-group.
-    Each figure is bytes read per launch / mean launch time (HIP events on the launch stream, launches back to
-    back, alternating input sets)."""
+def read_ceiling(meta, sets, partition, reps=20):
+    """HBM read ceilings on this GPU from the library's read probe (pkv_read_probe: the decode kernel's loads
+    and wave layout, with no arithmetic), over the benchmark's own rotating K/V pools:
+      decode_pattern   the decode's tiles in the decode's order: one work-group per (sequence, partition, head)
+                       with the head fastest, entries block_tables[s, j] * H + h of the partition's blocks, a
+                       ring of 2 stages (the decode kernel's own depth): the decode's gather without arithmetic;
+      random_tiles     every (block, head) tile of both pools once, in a random order, 128 per work-group;
+      sequential       both pools streamed from start to end, 128 tiles per work-group;
+      sequential_one_pool  the K pool alone, streamed, 4-stage ring;
+    random and sequential at ring depths 2 and 3.  Each figure is bytes read per launch / mean launch time
+    (HIP events on the launch stream, launches back to back, alternating input sets); "best" is the highest."""
     import torch
 
     import paged_kv_cache_383_amd as pkv
@@ -296,9 +298,14 @@ def read_ceiling(meta, sets, reps=20):
     pool_tiles = meta.num_blocks * H
     tab = sets[0].block_tables.long()
     B, M = tab.shape
-    h = torch.arange(H, device=dev, dtype=torch.int64)
-    order_dec = torch.where(tab[:, None, :] >= 0, tab[:, None, :] * H + h[None, :, None],
-                            torch.full_like(tab[:, None, :], -1)).reshape(B * H, M).to(torch.int32).contiguous()
+    pb = partition // bs if partition else M
+    P = -(-M // pb)
+    padded = torch.full((B, P * pb), -1, dtype=torch.int64, device=dev)
+    padded[:, :M] = tab
+    padded = padded.view(B, P, 1, pb)
+    h = torch.arange(H, device=dev, dtype=torch.int64).view(1, 1, H, 1)
+    order_dec = torch.where(padded >= 0, padded * H + h, torch.full_like(padded * H + h, -1))
+    order_dec = order_dec.reshape(B * P * H, pb).to(torch.int32).contiguous()
     n_dec = int((tab >= 0).sum().item()) * H
     g = torch.Generator(device=dev)
     g.manual_seed(383383)
@@ -306,11 +313,12 @@ def read_ceiling(meta, sets, reps=20):
     n_groups = -(-pool_tiles // group)
     order_rand = torch.full((n_groups * group,), -1, dtype=torch.int32, device=dev)
     order_rand[:pool_tiles] = torch.randperm(pool_tiles, generator=g, device=dev).to(torch.int32)
-    sink = torch.empty(8 * max(B * H, n_groups), dtype=torch.int32, device=dev)
+    sink = torch.empty(8 * max(B * P * H, n_groups), dtype=torch.int32, device=dev)
     R = len(sets)
 
-    def timed(order, group_tiles):
-        run = lambda i: pkv.read_probe(sets[i % R].k_cache, sets[i % R].v_cache, tile, order, group_tiles, sink)
+    def timed(order, group_tiles, depth, two=True):
+        run = lambda i: pkv.read_probe(sets[i % R].k_cache, sets[i % R].v_cache if two else None, tile, order,
+                                       group_tiles, sink, depth=depth)
         for i in range(3):
             run(i)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -321,14 +329,16 @@ def read_ceiling(meta, sets, reps=20):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps
 
-    us_dec = timed(order_dec, M)
-    us_rand = timed(order_rand, group)
-    us_seq = timed(None, group)
-    nbytes = {"decode_pattern": 2 * n_dec * tile, "random_tiles": 2 * pool_tiles * tile,
-              "sequential": 2 * pool_tiles * tile}
-    us = {"decode_pattern": us_dec, "random_tiles": us_rand, "sequential": us_seq}
-    out = {k: {"GB_per_s": round(nbytes[k] / us[k] / 1e3, 1), "mean_launch_us": round(us[k], 2),
-               "bytes_per_launch": nbytes[k]} for k in us}
+    both = 2 * pool_tiles * tile
+    runs = {"decode_pattern": (timed(order_dec, pb, 2), 2 * n_dec * tile)}
+    for d in (2, 3):
+        runs[f"random_tiles_depth{d}"] = (timed(order_rand, group, d), both)
+        runs[f"sequential_depth{d}"] = (timed(None, group, d), both)
+    runs["sequential_one_pool_depth4"] = (timed(None, group, 4, two=False), pool_tiles * tile)
+    out = {k: {"GB_per_s": round(b / us / 1e3, 1), "mean_launch_us": round(us, 2), "bytes_per_launch": b}
+           for k, (us, b) in runs.items()}
+    best = max(out, key=lambda k: out[k]["GB_per_s"])
+    out["best"] = {"pattern": best, "GB_per_s": out[best]["GB_per_s"]}
     out["tile_bytes"] = tile
     out["kernel"] = "read_probe_kernel (pkv_read_probe)"
     return out
@@ -833,8 +843,8 @@ def main():
 
     stream_ref = torch_stream_reference()
     log(f"plain PyTorch streaming on this GPU: {stream_ref}")
-    probe = read_ceiling(meta, sets)
-    probe["decode_call_over_decode_pattern_time"] = round(probe["decode_pattern"]["mean_launch_us"] / decode_us, 4)
+    probe = read_ceiling(meta, sets, resolved)
+    probe["decode_call_frac_of_best"] = round(achieved / probe["best"]["GB_per_s"], 4)
     log(f"read probe on this GPU: {probe}")
 
     cpu = None

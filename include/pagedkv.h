@@ -98,7 +98,7 @@ typedef enum {
  * Returns PKV_OK, or an error status with nothing launched.  num_tokens == 0
  * is a no-op.
  */
-int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64_t num_tokens,
+pkv_status paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64_t num_tokens,
                    void* k_cache, void* v_cache, int64_t num_blocks, int32_t num_heads,
                    int32_t head_dim, int32_t block_size, int32_t dtype, void* stream);
 
@@ -153,7 +153,7 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
  *                 contents needed; must not be shared by concurrent calls
  * Returns PKV_OK, or an error status with nothing launched.
  */
-int paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+pkv_status paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                            int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
@@ -192,7 +192,7 @@ int paged_attention_decode(const void* q, const void* k_cache, const void* v_cac
  * exceeds 65535, or (16-bit types) when the launch of one 256-thread
  * work-group per (sequence, head, 128-query tile) would exceed 2^32 threads.
  */
-int paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+pkv_status paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                             int32_t max_blocks_per_seq, const int32_t* query_start, const int32_t* context_lens,
                             int32_t num_seqs, int32_t max_query_len, int32_t num_heads, int32_t head_dim,
                             int32_t block_size, int64_t num_blocks, float scale, int32_t dtype, void* out,
@@ -215,7 +215,7 @@ int paged_attention_prefill(const void* q, const void* k_cache, const void* v_ca
  * with an id outside [0, num_blocks) is skipped by the kernel.  Returns PKV_OK,
  * or an error status with nothing launched.  num_pairs == 0 is a no-op.
  */
-int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int64_t num_pairs,
+pkv_status paged_kv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int64_t num_pairs,
                          int64_t num_blocks, int32_t num_heads, int32_t head_dim, int32_t block_size,
                          int32_t dtype, void* stream);
 
@@ -238,7 +238,7 @@ int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
  * the arrays are skipped; a row whose length or block id is out of range gets
  * slot -1.  Returns PKV_OK, or an error status with nothing launched.
  */
-int paged_kv_prepare_step(int32_t* block_tables, int32_t max_blocks_per_seq, int32_t* context_lens, int32_t num_seqs,
+pkv_status paged_kv_prepare_step(int32_t* block_tables, int32_t max_blocks_per_seq, int32_t* context_lens, int32_t num_seqs,
                           const int32_t* updates, int64_t num_updates, const int32_t* new_lens,
                           int64_t* slot_mapping, int32_t block_size, int64_t num_blocks, void* stream);
 
@@ -260,7 +260,7 @@ int paged_kv_prepare_step(int32_t* block_tables, int32_t max_blocks_per_seq, int
  *   v_cache       written at the newest slots, read everywhere else
  * Other arguments, ownership and errors as for paged_attention_decode.
  */
-int paged_attention_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+pkv_status paged_attention_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                 int32_t block_size, int64_t num_blocks, float scale, int32_t dtype, void* out,
@@ -284,7 +284,7 @@ int paged_attention_decode_step(const void* q, const void* k_new, const void* v_
  * host threads) race with each other; the caller must order them.
  */
 #define PKV_NOALLOC_SCRATCH_BYTES (16u << 20)
-int paged_attention_decode_step_noalloc(const void* q, const void* k_new, const void* v_new, void* k_cache,
+pkv_status paged_attention_decode_step_noalloc(const void* q, const void* k_new, const void* v_new, void* k_cache,
                                         void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
                                         const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                                         int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
@@ -322,11 +322,11 @@ void pkv_pool_destroy(pkv_block_pool* pool);
 
 /* New sequence `seq` holding num_tokens tokens in ceil(num_tokens / block_size)
  * fresh blocks ([explain] Step 6: blocks are allocated at the start of prefill). */
-int pkv_pool_allocate(pkv_block_pool* pool, int64_t seq, int64_t num_tokens);
+pkv_status pkv_pool_allocate(pkv_block_pool* pool, int64_t seq, int64_t num_tokens);
 
 /* New sequence `child` sharing all of `parent`'s blocks (each gains a
  * reference): a shared prompt prefix or parallel samples ([explain] Step 9). */
-int pkv_pool_fork(pkv_block_pool* pool, int64_t parent, int64_t child);
+pkv_status pkv_pool_fork(pkv_block_pool* pool, int64_t parent, int64_t child);
 
 /* Reserve slots for n new tokens of `seq`.  slots_out[n] receives each token's
  * flat slot (block * block_size + offset) for paged_kv_write.  A new block is
@@ -334,7 +334,7 @@ int pkv_pool_fork(pkv_block_pool* pool, int64_t parent, int64_t child);
  * last block is shared, it is replaced by a fresh block and the pair (old, new)
  * goes to copies_out (int64 [max_copies, 2]); *num_copies receives the count
  * (0 or 1).  The copies must run (paged_kv_copy_blocks) before the write. */
-int pkv_pool_append_slots(pkv_block_pool* pool, int64_t seq, int64_t n, int64_t* slots_out,
+pkv_status pkv_pool_append_slots(pkv_block_pool* pool, int64_t seq, int64_t n, int64_t* slots_out,
                           int64_t* copies_out, int64_t max_copies, int64_t* num_copies);
 
 /* Flat slots (block * block_size + offset) of tokens first .. first + n - 1 of
@@ -343,15 +343,15 @@ int pkv_pool_append_slots(pkv_block_pool* pool, int64_t seq, int64_t n, int64_t*
  * of a request sits at offset t % block_size of the block its table lists at
  * t / block_size).  PKV_EINVAL for an unknown sequence or tokens it does not
  * hold. */
-int pkv_pool_slots(const pkv_block_pool* pool, int64_t seq, int64_t first, int64_t n, int64_t* slots_out);
+pkv_status pkv_pool_slots(const pkv_block_pool* pool, int64_t seq, int64_t first, int64_t n, int64_t* slots_out);
 
 /* Drop `seq`; blocks no other table holds return to the free list ([explain]
  * Step 7: released blocks are immediately reusable). */
-int pkv_pool_free(pkv_block_pool* pool, int64_t seq);
+pkv_status pkv_pool_free(pkv_block_pool* pool, int64_t seq);
 
 /* Padded int32 block tables [n, width] (unused entries -1) and int32 context
  * lengths [n] of the listed sequences, ready for paged_attention_decode. */
-int pkv_pool_build_tables(const pkv_block_pool* pool, const int64_t* seqs, int32_t n, int32_t width,
+pkv_status pkv_pool_build_tables(const pkv_block_pool* pool, const int64_t* seqs, int32_t n, int32_t width,
                           int32_t* tables_out, int32_t* lens_out);
 
 /* Queries: free block count; a block's reference count (-1 for a bad id);
@@ -378,7 +378,7 @@ typedef struct {
   int64_t allocated_slots;  /* used_blocks * block_size                                   */
   int64_t shared_blocks;    /* used blocks held by more than one table                    */
 } pkv_pool_usage_t;
-int pkv_pool_usage(const pkv_block_pool* pool, pkv_pool_usage_t* out);
+pkv_status pkv_pool_usage(const pkv_block_pool* pool, pkv_pool_usage_t* out);
 
 /* The waste comparison derived from pkv_pool_usage ([explain] the step-6
  * calculation: static reservation of max_model_len slots per request against
@@ -393,13 +393,13 @@ typedef struct {
   int64_t stored_bytes;     /* stored_tokens * bytes_per_token                                */
   int64_t static_bytes;     /* static_slots * bytes_per_token                                 */
 } pkv_waste_t;
-int pkv_pool_waste(const pkv_block_pool* pool, int64_t max_model_len, int64_t bytes_per_token, pkv_waste_t* out);
+pkv_status pkv_pool_waste(const pkv_block_pool* pool, int64_t max_model_len, int64_t bytes_per_token, pkv_waste_t* out);
 
 /* Usage and waste of n requests of the given lengths, each with `samples`
  * parallel samples sharing its prompt ([explain] Step 9), in a pool of exactly
  * the blocks the prompts need (request i is allocated as sequence i * samples
  * and forked samples - 1 times). */
-int pkv_account(const int64_t* lens, int32_t n, int32_t block_size, int32_t samples, int64_t max_model_len,
+pkv_status pkv_account(const int64_t* lens, int32_t n, int32_t block_size, int32_t samples, int64_t max_model_len,
                 int64_t bytes_per_token, pkv_pool_usage_t* usage_out, pkv_waste_t* waste_out);
 
 /*
@@ -422,7 +422,7 @@ void pkv_batch_destroy(pkv_batch* batch);
 
 /* Row `row` now runs sequence `seq` (which must exist in the pool and fit in
  * `width` blocks), or is idle when seq < 0.  Takes effect at the next plan. */
-int pkv_batch_set_row(pkv_batch* batch, int32_t row, int64_t seq);
+pkv_status pkv_batch_set_row(pkv_batch* batch, int32_t row, int64_t seq);
 
 /* One step's bookkeeping.  Every non-idle row's sequence grows by
  * tokens_per_row tokens (pkv_pool_append_slots; 1 for a decode step, 0 to only
@@ -433,7 +433,7 @@ int pkv_batch_set_row(pkv_batch* batch, int32_t row, int64_t seq);
  * Upload updates and lens, then paged_kv_prepare_step, paged_kv_copy_blocks,
  * paged_kv_write and paged_attention_decode.  PKV_ENOSPACE (too few free
  * blocks) and PKV_EINVAL leave the pool and the batch unchanged. */
-int pkv_batch_plan_step(pkv_batch* batch, int32_t tokens_per_row, int32_t* updates_out, int64_t max_updates,
+pkv_status pkv_batch_plan_step(pkv_batch* batch, int32_t tokens_per_row, int32_t* updates_out, int64_t max_updates,
                         int64_t* n_updates, int32_t* lens_out, int64_t* copies_out, int64_t max_copies,
                         int64_t* n_copies);
 

@@ -20,6 +20,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pagedkv.h"
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -37,21 +39,24 @@ extern "C" {
  *   num_groups    work-groups; group g reads entries g*group_tiles ..
  *                 (g+1)*group_tiles - 1 of the order
  *   group_tiles   entries per work-group (>= 1)
+ *   depth         stages in the ring of stage buffers: 2 or 3 with two pools, 2 to 4
+ *                 with one (depth - 1 stages of loads in flight while one is folded)
  *   sink          uint32 [num_groups * 8], written: one XOR of the data per
  *                 wave, so that no load can be dropped
  *
  * Work decomposition, as in the decode kernel: 8 wave64 per work-group; a
  * wave works in stages of 8 KiB per pool (two 4 KiB tiles or one 8 KiB tile),
  * wave w taking stages w, w + 8, ... of its group; 16-byte non-temporal
- * buffer loads per lane, two stages of both pools in flight per wave.  With
+ * buffer loads per lane.  With depth 2 this is the decode kernel's own load
+ * depth for 16-bit tiles; deeper rings show what more loads in flight give.  With
  * the decode's own tile order (group = (sequence, head) row, entries =
  * block_tables[s, j] * num_heads + h, padded with -1) this is the decode's
  * gather with the arithmetic removed; with a random permutation it is a
  * random-tile read; with order NULL a sequential stream.
  * Bytes read per call = (1 or 2 pools) * tile_bytes * number of valid entries.
  */
-int pkv_read_probe(const void* a, const void* b, int64_t pool_tiles, int32_t tile_bytes, const int32_t* order,
-                   int32_t num_groups, int32_t group_tiles, uint32_t* sink, void* stream);
+pkv_status pkv_read_probe(const void* a, const void* b, int64_t pool_tiles, int32_t tile_bytes, const int32_t* order,
+                   int32_t num_groups, int32_t group_tiles, int32_t depth, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

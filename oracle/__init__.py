@@ -7,5 +7,5 @@ counts, copy-on-write, freeing) and the block copy.
 """
 from .oracle import (  # noqa: F401
     BF16, F16, F32, attend, blocks_needed, decode, decode_split, gather_sequence, kv_write,
-    lse_merge, newest_token_slots, partition_state, prefill, round_to_storage, slot_to_block_offset, to_float64,
+    lse_merge, newest_token_slots, partition_state, prefill, slot_to_block_offset, to_float64,
 )

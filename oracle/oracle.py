@@ -231,21 +231,3 @@ def decode_split(q, k_cache, v_cache, block_tables, context_lens, scale: float, 
                   for a in range(0, L, partition_size)]
         out[i] = lse_merge(states)
     return out
-
-
-def round_to_storage(x, dtype: str) -> np.ndarray:
-    """Round float64 values to the storage dtype (round-to-nearest-even), as float64.
-
-    Used to express the output's own rounding in tolerances; fp32 and fp16 use
-    NumPy's IEEE casts, bf16 rounds the binary32 bit pattern to its top half.
-    """
-    x = np.asarray(x, dtype=np.float64)
-    if dtype == F32:
-        return x.astype(np.float32).astype(np.float64)
-    if dtype == F16:
-        return x.astype(np.float16).astype(np.float64)
-    if dtype == BF16:
-        u = x.astype(np.float32).view(np.uint32).astype(np.uint64)
-        u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-        return to_float64(u.astype(np.uint16), BF16)
-    raise ValueError(dtype)

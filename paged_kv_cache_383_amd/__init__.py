@@ -36,7 +36,9 @@ STATUS_NAMES = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWO
 PARTITION_AUTO = -1            # let the library choose the split-context partition
 DEFAULT_PARTITION = PARTITION_AUTO
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpagedkv.so")
+# PKV_LIBRARY names another build of the same sources to load instead (the host-only sanitizer build).
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib",
+                                                         "libpagedkv.so")
 _lib = None
 
 
@@ -91,7 +93,7 @@ def lib() -> ctypes.CDLL:
             "pkv_batch_set_row": ([vp, i32, i64], ctypes.c_int),
             "pkv_batch_plan_step": ([vp, i32, vp, i64, vp, vp, vp, i64, vp], ctypes.c_int),
             "paged_kv_prepare_step": ([vp, i32, vp, i32, vp, i64, vp, vp, i32, i64, vp], ctypes.c_int),
-            "pkv_read_probe": ([vp, vp, i64, i32, vp, i32, i32, vp, vp], ctypes.c_int),
+            "pkv_read_probe": ([vp, vp, i64, i32, vp, i32, i32, i32, vp, vp], ctypes.c_int),
             "paged_attention_decode_step_noalloc": ([vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i64,
                                                      ctypes.c_float, i32, vp, i32, vp], ctypes.c_int),
         }
@@ -290,10 +292,10 @@ def paged_attention_decode_step_noalloc(q, k_new, v_new, k_cache, v_cache, block
 NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
-def read_probe(a, b, tile_bytes: int, order, group_tiles: int, sink, num_groups=None):
+def read_probe(a, b, tile_bytes: int, order, group_tiles: int, sink, num_groups=None, depth: int = 2):
     """Diagnostic HBM read (include/pagedkv_probe.h): tiles of ``tile_bytes`` of pools ``a`` and ``b`` (b may be
-    None) in the order of the int32 tensor ``order`` (None: sequential), ``group_tiles`` entries per work-group;
-    ``sink`` int32 receives one word per wave."""
+    None) in the order of the int32 tensor ``order`` (None: sequential), ``group_tiles`` entries per work-group,
+    a ring of ``depth`` stages per wave; ``sink`` int32 receives one word per wave."""
     import torch
     _device_tensor("a", a)
     if b is not None:
@@ -315,7 +317,7 @@ def read_probe(a, b, tile_bytes: int, order, group_tiles: int, sink, num_groups=
         raise ValueError("sink needs 8 words per work-group")
     _check(_launch(a.device, lib().pkv_read_probe, a.data_ptr(), None if b is None else b.data_ptr(), pool_tiles,
                    int(tile_bytes), None if order is None else order.data_ptr(), int(groups), int(group_tiles),
-                   sink.data_ptr()))
+                   int(depth), sink.data_ptr()))
     return groups
 
 

@@ -19,24 +19,24 @@ thread_local std::string g_last_error;
 
 }  // namespace
 
-int pkv::set_error(int code, const std::string& message) {
+pkv_status pkv::set_error(int code, const std::string& message) {
   g_last_error = message;
-  return code;
+  return static_cast<pkv_status>(code);
 }
 
 namespace {
 
-int fail(int code, const char* fmt, ...) {
+pkv_status fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(buf, sizeof(buf), fmt, ap);
   va_end(ap);
   g_last_error = buf;
-  return code;
+  return static_cast<pkv_status>(code);
 }
 
-int ok() {
+pkv_status ok() {
   g_last_error.clear();
   return PKV_OK;
 }
@@ -49,7 +49,7 @@ bool debug_checks() {
 int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : 2; }
 
 // Shared shape checks of both calls.
-int check_shape(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t block_size,
+pkv_status check_shape(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t block_size,
                 int64_t num_blocks) {
   if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16)
     return fail(PKV_EUNSUPPORTED, "dtype %d is not PKV_F32, PKV_F16 or PKV_BF16", dtype);
@@ -68,7 +68,7 @@ int check_shape(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t bloc
 // Element arrays move in 16-byte vectors; metadata is read in whole words.
 bool misaligned(const void* p, uintptr_t n) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & (n - 1)) != 0; }
 
-int hip_fail(hipError_t e, const char* what) {
+pkv_status hip_fail(hipError_t e, const char* what) {
   return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
@@ -123,12 +123,12 @@ extern "C" size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_
   return pkv::workspace_layout(num_seqs, num_heads, head_dim, partitions_for(max_blocks_per_seq, pb)).bytes;
 }
 
-extern "C" int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping,
+extern "C" pkv_status paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping,
                               int64_t num_tokens, void* k_cache, void* v_cache, int64_t num_blocks,
                               int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
                               void* stream) {
   if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens must be >= 0 (got %lld)", (long long)num_tokens);
-  if (int rc = check_shape(dtype, num_heads, head_dim, block_size, num_blocks)) return rc;
+  if (pkv_status rc = check_shape(dtype, num_heads, head_dim, block_size, num_blocks)) return rc;
   if (num_tokens == 0) return ok();
   if (!k || !v || !slot_mapping || !k_cache || !v_cache)
     return fail(PKV_EINVAL, "null pointer among k, v, slot_mapping, k_cache, v_cache");
@@ -160,11 +160,11 @@ extern "C" int paged_kv_write(const void* k, const void* v, const int64_t* slot_
   return ok();
 }
 
-extern "C" int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+extern "C" pkv_status paged_kv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
                                     int64_t num_pairs, int64_t num_blocks, int32_t num_heads,
                                     int32_t head_dim, int32_t block_size, int32_t dtype, void* stream) {
   if (num_pairs < 0) return fail(PKV_EINVAL, "num_pairs must be >= 0 (got %lld)", (long long)num_pairs);
-  if (int rc = check_shape(dtype, num_heads, head_dim, block_size, num_blocks)) return rc;
+  if (pkv_status rc = check_shape(dtype, num_heads, head_dim, block_size, num_blocks)) return rc;
   if (num_pairs == 0) return ok();
   if (!k_cache || !v_cache || !block_mapping)
     return fail(PKV_EINVAL, "null pointer among k_cache, v_cache, block_mapping");
@@ -196,7 +196,7 @@ extern "C" int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int64_t*
   return ok();
 }
 
-extern "C" int paged_kv_prepare_step(int32_t* block_tables, int32_t max_blocks_per_seq, int32_t* context_lens,
+extern "C" pkv_status paged_kv_prepare_step(int32_t* block_tables, int32_t max_blocks_per_seq, int32_t* context_lens,
                                      int32_t num_seqs, const int32_t* updates, int64_t num_updates,
                                      const int32_t* new_lens, int64_t* slot_mapping, int32_t block_size,
                                      int64_t num_blocks, void* stream) {
@@ -217,14 +217,14 @@ extern "C" int paged_kv_prepare_step(int32_t* block_tables, int32_t max_blocks_p
   return ok();
 }
 
-extern "C" int paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
+extern "C" pkv_status paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                                        const int32_t* query_start, const int32_t* context_lens, int32_t num_seqs,
                                        int32_t max_query_len, int32_t num_heads, int32_t head_dim,
                                        int32_t block_size, int64_t num_blocks, float scale, int32_t dtype,
                                        void* out, void* stream) {
   if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs must be >= 0 (got %d)", num_seqs);
-  if (int rc = check_shape(dtype, num_heads, head_dim, block_size, num_blocks)) return rc;
+  if (pkv_status rc = check_shape(dtype, num_heads, head_dim, block_size, num_blocks)) return rc;
   if (max_blocks_per_seq <= 0)
     return fail(PKV_EINVAL, "max_blocks_per_seq must be positive (got %d)", max_blocks_per_seq);
   if (int64_t(max_blocks_per_seq) * block_size > INT32_MAX)
@@ -298,13 +298,13 @@ namespace {
 // non-null: the fused step).
 // With static_scratch the split-context partials go to the library's own
 // per-device array (pkv::static_scratch) instead of a caller workspace.
-int decode_common(const void* q, const void* k_new, const void* v_new, const void* k_cache, const void* v_cache,
+pkv_status decode_common(const void* q, const void* k_new, const void* v_new, const void* k_cache, const void* v_cache,
                   const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                   int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                   float scale, int32_t dtype, void* out, void* workspace, size_t workspace_bytes,
                   int32_t partition_size, void* stream, bool static_scratch = false) {
   if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs must be >= 0 (got %d)", num_seqs);
-  if (int rc = check_shape(dtype, num_heads, head_dim, block_size, num_blocks)) return rc;
+  if (pkv_status rc = check_shape(dtype, num_heads, head_dim, block_size, num_blocks)) return rc;
   if (max_blocks_per_seq <= 0)
     return fail(PKV_EINVAL, "max_blocks_per_seq must be positive (got %d)", max_blocks_per_seq);
   if (int64_t(max_blocks_per_seq) * block_size > INT32_MAX)
@@ -387,7 +387,7 @@ int decode_common(const void* q, const void* k_new, const void* v_new, const voi
 
 }  // namespace
 
-extern "C" int paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+extern "C" pkv_status paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                                       int32_t head_dim, int32_t block_size, int64_t num_blocks,
@@ -398,7 +398,7 @@ extern "C" int paged_attention_decode(const void* q, const void* k_cache, const 
                        workspace_bytes, partition_size, stream);
 }
 
-extern "C" int paged_attention_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+extern "C" pkv_status paged_attention_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
                                            void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
                                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                                            int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
@@ -410,7 +410,7 @@ extern "C" int paged_attention_decode_step(const void* q, const void* k_new, con
                        workspace_bytes, partition_size, stream);
 }
 
-extern "C" int paged_attention_decode_step_noalloc(const void* q, const void* k_new, const void* v_new,
+extern "C" pkv_status paged_attention_decode_step_noalloc(const void* q, const void* k_new, const void* v_new,
                                                    void* k_cache, void* v_cache, const int32_t* block_tables,
                                                    int32_t max_blocks_per_seq, const int32_t* context_lens,
                                                    int32_t num_seqs, int32_t num_heads, int32_t head_dim,

@@ -30,7 +30,7 @@
 
 namespace {
 
-int pool_fail(int code, const std::string& msg) { return pkv::set_error(code, msg); }
+pkv_status pool_fail(int code, const std::string& msg) { return pkv::set_error(code, msg); }
 
 struct Sequence {
   std::vector<int32_t> table;
@@ -90,7 +90,7 @@ extern "C" pkv_block_pool* pkv_pool_create(int64_t num_blocks, int32_t block_siz
 
 extern "C" void pkv_pool_destroy(pkv_block_pool* p) { delete p; }
 
-extern "C" int pkv_pool_allocate(pkv_block_pool* p, int64_t seq, int64_t num_tokens) {
+extern "C" pkv_status pkv_pool_allocate(pkv_block_pool* p, int64_t seq, int64_t num_tokens) {
   if (!p || num_tokens < 0) return pool_fail(PKV_EINVAL, "null pool or negative token count");
   if (p->seqs.count(seq)) return pool_fail(PKV_EINVAL, "sequence " + std::to_string(seq) + " already exists");
   const int64_t need = p->blocks_for(num_tokens);
@@ -105,7 +105,7 @@ extern "C" int pkv_pool_allocate(pkv_block_pool* p, int64_t seq, int64_t num_tok
   return pkv::set_error(PKV_OK, "");
 }
 
-extern "C" int pkv_pool_fork(pkv_block_pool* p, int64_t parent, int64_t child) {
+extern "C" pkv_status pkv_pool_fork(pkv_block_pool* p, int64_t parent, int64_t child) {
   if (!p) return pool_fail(PKV_EINVAL, "null pool");
   auto it = p->seqs.find(parent);
   if (it == p->seqs.end()) return pool_fail(PKV_EINVAL, "unknown sequence " + std::to_string(parent));
@@ -116,7 +116,7 @@ extern "C" int pkv_pool_fork(pkv_block_pool* p, int64_t parent, int64_t child) {
   return pkv::set_error(PKV_OK, "");
 }
 
-extern "C" int pkv_pool_append_slots(pkv_block_pool* p, int64_t seq, int64_t n, int64_t* slots_out,
+extern "C" pkv_status pkv_pool_append_slots(pkv_block_pool* p, int64_t seq, int64_t n, int64_t* slots_out,
                                      int64_t* copies_out, int64_t max_copies, int64_t* num_copies) {
   if (!p || n < 0 || (n > 0 && !slots_out) || !num_copies)
     return pool_fail(PKV_EINVAL, "null pool, output pointer or negative count");
@@ -155,7 +155,7 @@ extern "C" int pkv_pool_append_slots(pkv_block_pool* p, int64_t seq, int64_t n, 
   return pkv::set_error(PKV_OK, "");
 }
 
-extern "C" int pkv_pool_slots(const pkv_block_pool* p, int64_t seq, int64_t first, int64_t n, int64_t* slots_out) {
+extern "C" pkv_status pkv_pool_slots(const pkv_block_pool* p, int64_t seq, int64_t first, int64_t n, int64_t* slots_out) {
   if (!p || n < 0 || first < 0 || (n > 0 && !slots_out))
     return pool_fail(PKV_EINVAL, "null pool or output, or negative position or count");
   auto it = p->seqs.find(seq);
@@ -171,7 +171,7 @@ extern "C" int pkv_pool_slots(const pkv_block_pool* p, int64_t seq, int64_t firs
   return pkv::set_error(PKV_OK, "");
 }
 
-extern "C" int pkv_pool_free(pkv_block_pool* p, int64_t seq) {
+extern "C" pkv_status pkv_pool_free(pkv_block_pool* p, int64_t seq) {
   if (!p) return pool_fail(PKV_EINVAL, "null pool");
   auto it = p->seqs.find(seq);
   if (it == p->seqs.end()) return pool_fail(PKV_EINVAL, "unknown sequence " + std::to_string(seq));
@@ -211,7 +211,7 @@ extern "C" int64_t pkv_pool_free_list(const pkv_block_pool* p, int32_t* out, int
   return int64_t(p->free_list.size());
 }
 
-extern "C" int pkv_pool_usage(const pkv_block_pool* p, pkv_pool_usage_t* out) {
+extern "C" pkv_status pkv_pool_usage(const pkv_block_pool* p, pkv_pool_usage_t* out) {
   if (!p || !out) return pool_fail(PKV_EINVAL, "null pool or output");
   // A used block stores the filled slots of its fullest holder, once, however
   // many tables share it.
@@ -243,12 +243,12 @@ extern "C" int pkv_pool_usage(const pkv_block_pool* p, pkv_pool_usage_t* out) {
   return pkv::set_error(PKV_OK, "");
 }
 
-extern "C" int pkv_pool_waste(const pkv_block_pool* p, int64_t max_model_len, int64_t bytes_per_token,
+extern "C" pkv_status pkv_pool_waste(const pkv_block_pool* p, int64_t max_model_len, int64_t bytes_per_token,
                               pkv_waste_t* out) {
   if (!p || !out || max_model_len < 0 || bytes_per_token < 0)
     return pool_fail(PKV_EINVAL, "null pool or output, or negative max_model_len / bytes_per_token");
   pkv_pool_usage_t u{};
-  if (int rc = pkv_pool_usage(p, &u)) return rc;
+  if (pkv_status rc = pkv_pool_usage(p, &u)) return rc;
   pkv_waste_t w{};
   w.empty_slots = u.allocated_slots - u.stored_tokens;
   w.paged_waste = u.allocated_slots ? double(w.empty_slots) / double(u.allocated_slots) : 0.0;
@@ -261,7 +261,7 @@ extern "C" int pkv_pool_waste(const pkv_block_pool* p, int64_t max_model_len, in
   return pkv::set_error(PKV_OK, "");
 }
 
-extern "C" int pkv_account(const int64_t* lens, int32_t n, int32_t block_size, int32_t samples,
+extern "C" pkv_status pkv_account(const int64_t* lens, int32_t n, int32_t block_size, int32_t samples,
                            int64_t max_model_len, int64_t bytes_per_token, pkv_pool_usage_t* usage_out,
                            pkv_waste_t* waste_out) {
   if (n < 0 || (n > 0 && !lens) || block_size <= 0 || samples < 1 || !usage_out || !waste_out)
@@ -275,7 +275,7 @@ extern "C" int pkv_account(const int64_t* lens, int32_t n, int32_t block_size, i
   // Exactly the blocks the prompts need: forks share them and allocate nothing.
   pkv_block_pool* p = pkv_pool_create(std::max<int64_t>(need, 1), block_size, nullptr);
   if (!p) return pool_fail(PKV_EINVAL, "out of host memory");
-  int rc = PKV_OK;
+  pkv_status rc = PKV_OK;
   for (int32_t i = 0; i < n && rc == PKV_OK; ++i) {
     rc = pkv_pool_allocate(p, int64_t(i) * samples, lens[i]);
     for (int32_t s = 1; s < samples && rc == PKV_OK; ++s)
@@ -287,7 +287,7 @@ extern "C" int pkv_account(const int64_t* lens, int32_t n, int32_t block_size, i
   return rc;
 }
 
-extern "C" int pkv_pool_build_tables(const pkv_block_pool* p, const int64_t* seqs, int32_t n, int32_t width,
+extern "C" pkv_status pkv_pool_build_tables(const pkv_block_pool* p, const int64_t* seqs, int32_t n, int32_t width,
                                      int32_t* tables_out, int32_t* lens_out) {
   if (!p || n < 0 || width <= 0 || (n > 0 && (!seqs || !tables_out || !lens_out)))
     return pool_fail(PKV_EINVAL, "null pool or output, or non-positive width");
@@ -351,7 +351,7 @@ extern "C" pkv_batch* pkv_batch_create(pkv_block_pool* pool, int32_t rows, int32
 
 extern "C" void pkv_batch_destroy(pkv_batch* b) { delete b; }
 
-extern "C" int pkv_batch_set_row(pkv_batch* b, int32_t row, int64_t seq) {
+extern "C" pkv_status pkv_batch_set_row(pkv_batch* b, int32_t row, int64_t seq) {
   if (!b || row < 0 || row >= b->rows) return pool_fail(PKV_EINVAL, "null batch or row out of range");
   if (seq >= 0) {
     auto it = b->pool->seqs.find(seq);
@@ -364,7 +364,7 @@ extern "C" int pkv_batch_set_row(pkv_batch* b, int32_t row, int64_t seq) {
   return pkv::set_error(PKV_OK, "");
 }
 
-extern "C" int pkv_batch_plan_step(pkv_batch* b, int32_t tokens_per_row, int32_t* updates_out, int64_t max_updates,
+extern "C" pkv_status pkv_batch_plan_step(pkv_batch* b, int32_t tokens_per_row, int32_t* updates_out, int64_t max_updates,
                                    int64_t* n_updates, int32_t* lens_out, int64_t* copies_out, int64_t max_copies,
                                    int64_t* n_copies) {
   if (!b || tokens_per_row < 0 || !n_updates || !lens_out || !n_copies || !updates_out ||

@@ -350,11 +350,15 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
   };
 
   // Before the owner wave issues the loads of stage i_new, the newest row's
-  // store has completed.  Vector memory operations retire in order on gfx9,
-  // stores included, and the store is older than every stage load, so it is
-  // enough to wait until no more than the loads of the stages issued since
-  // are outstanding: min(i, NST - 1) stages (later ones than that have been
-  // consumed, hence waited for, already).  For i = 0 nothing has been issued
+  // store has completed.  On gfx9-family GPUs (CDNA included) one vector
+  // memory counter covers a wave's loads and stores, and it counts them down
+  // in the order they were issued, a store once its data has reached the L2
+  // cache (AMD's CDNA3 and CDNA4 ISA reference guides, section "Data
+  // Dependency Resolution", the S_WAITCNT vector-memory counter).  The store
+  // is older than every stage load, so it is enough to wait until no more
+  // than the loads of the stages issued since are outstanding: min(i, NST - 1)
+  // stages (later ones than that have been consumed, hence waited for,
+  // already).  For i = 0 nothing has been issued
   // since, and the wait is for everything.  For any other stage, and any
   // other wave, this is not reached.
   constexpr int kLoadsPerStage = 2 * TPS * G::kLoads;

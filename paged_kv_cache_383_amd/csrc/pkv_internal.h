@@ -9,11 +9,13 @@
 
 #include <string>
 
+#include "pagedkv.h"
+
 namespace pkv {
 
 // Records the calling thread's last status text (read by pkv_last_error) and
 // returns `code`.
-int set_error(int code, const std::string& message);
+pkv_status set_error(int code, const std::string& message);
 
 // Split-context workspace: three fp32 arrays, each 256-byte aligned.
 //   m    [num_seqs, num_heads, P]      running max of a partition (base-2 logits)

@@ -8,9 +8,9 @@
 // arithmetic: 8 wave64 per work-group, stages of 8 KiB per pool, wave w
 // taking stages w, w + 8, ..., a buffer resource per tile (an invalid tile
 // gets an empty one: its loads return zeros and touch nothing), 16-byte
-// non-temporal loads per lane, and a 2-deep ring of stage buffers in
-// registers so that one stage's loads are in flight while the other is
-// folded.  Folding is an XOR of the loaded words, written out once per wave.
+// non-temporal loads per lane, and a ring of `depth` stage buffers in
+// registers so that depth - 1 stages' loads are in flight while one is
+// folded (the decode kernel's 16-bit kernels hold two stages).  Folding is an XOR of the loaded words, written out once per wave.
 // The loop body has no branch (the tile index is a select), so it is one basic
 // block and every wait in it leaves a whole stage in flight; with a branch in
 // the index the register allocator moved one stage buffer at the back edge,
@@ -29,11 +29,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 8;
 constexpr int kStageBytes = 8192;              // per pool, as the decode kernel's 16-bit stages
 constexpr int kLoadsPerStage = kStageBytes / 1024;
-constexpr int kRing = 2;
 constexpr int kNonTemporal = 2;                // buffer-load aux bit the decode kernel uses for K/V tiles
 constexpr int kBufferWord3 = 0x00020000;       // raw buffer resource: 32-bit data format, no swizzle
 
-template <int TILE, bool TWO, bool ORDERED>
+template <int TILE, bool TWO, bool ORDERED, int DEPTH>
 __global__ __launch_bounds__(64 * kWaves) void read_probe_kernel(const char* __restrict__ a,
                                                                  const char* __restrict__ b, int64_t pool_tiles,
                                                                  const int32_t* __restrict__ order,
@@ -88,20 +87,23 @@ __global__ __launch_bounds__(64 * kWaves) void read_probe_kernel(const char* __r
   };
 
   // Same loop shape as the decode kernel: step s issues stage s into buffer
-  // s % kRing and folds stage s - 1; the first step folds zeroed buffers and
-  // the last issues empty loads.
+  // s % DEPTH and folds stage s - (DEPTH - 1); the first steps fold zeroed
+  // buffers and the last ones issue empty loads.
   if (n_my > 0) {
-    u32x4 ba[kRing][kLoadsPerStage], bb[kRing][kLoadsPerStage];
+    u32x4 ba[DEPTH][kLoadsPerStage], bb[TWO ? DEPTH : 1][kLoadsPerStage];
 #pragma unroll
-    for (int r = 0; r < kRing; ++r)
+    for (int r = 0; r < DEPTH; ++r)
 #pragma unroll
-      for (int i = 0; i < kLoadsPerStage; ++i) ba[r][i] = bb[r][i] = u32x4{0u, 0u, 0u, 0u};
-    for (int i = 0; i < n_my + kRing - 1; i += kRing) {
+      for (int i = 0; i < kLoadsPerStage; ++i) {
+        ba[r][i] = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (TWO) bb[r][i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    for (int i = 0; i < n_my + DEPTH - 1; i += DEPTH) {
 #pragma unroll
-      for (int r = 0; r < kRing; ++r) {
-        issue(ba[r], bb[r], i + r);
+      for (int r = 0; r < DEPTH; ++r) {
+        issue(ba[r], bb[TWO ? r : 0], i + r);
         __builtin_amdgcn_sched_barrier(0);
-        fold(ba[(r + 1) % kRing], bb[(r + 1) % kRing]);
+        fold(ba[(r + 1) % DEPTH], bb[TWO ? (r + 1) % DEPTH : 0]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -111,22 +113,38 @@ __global__ __launch_bounds__(64 * kWaves) void read_probe_kernel(const char* __r
   if (lane == 0) sink[int64_t(blockIdx.x) * kWaves + wave] = x;
 }
 
-template <int TILE>
-hipError_t launch_tile(const void* a, const void* b, int64_t pool_tiles, const int32_t* order, int32_t num_groups,
-                       int32_t group_tiles, uint32_t* sink, hipStream_t stream) {
-  auto* kernel = b != nullptr ? (order != nullptr ? read_probe_kernel<TILE, true, true> : read_probe_kernel<TILE, true, false>)
-                               : (order != nullptr ? read_probe_kernel<TILE, false, true> : read_probe_kernel<TILE, false, false>);
+template <int TILE, bool TWO, bool ORDERED>
+hipError_t launch_depth(int depth, const void* a, const void* b, int64_t pool_tiles, const int32_t* order,
+                        int32_t num_groups, int32_t group_tiles, uint32_t* sink, hipStream_t stream) {
+  // Two pools stop at depth 3: a fourth pair of stage buffers does not fit the registers.
+  void (*kernel)(const char*, const char*, int64_t, const int32_t*, int32_t, uint32_t*) =
+      depth == 2 ? read_probe_kernel<TILE, TWO, ORDERED, 2> : read_probe_kernel<TILE, TWO, ORDERED, 3>;
+  if constexpr (!TWO) {
+    if (depth == 4) kernel = read_probe_kernel<TILE, TWO, ORDERED, 4>;
+  }
   hipLaunchKernelGGL(kernel, dim3(unsigned(num_groups)), dim3(64 * kWaves), 0, stream,
                      static_cast<const char*>(a), static_cast<const char*>(b), pool_tiles, order, group_tiles, sink);
   return hipGetLastError();
 }
 
+template <int TILE>
+hipError_t launch_tile(int depth, const void* a, const void* b, int64_t pool_tiles, const int32_t* order,
+                       int32_t num_groups, int32_t group_tiles, uint32_t* sink, hipStream_t stream) {
+  if (b != nullptr)
+    return order != nullptr
+               ? launch_depth<TILE, true, true>(depth, a, b, pool_tiles, order, num_groups, group_tiles, sink, stream)
+               : launch_depth<TILE, true, false>(depth, a, b, pool_tiles, order, num_groups, group_tiles, sink, stream);
+  return order != nullptr
+             ? launch_depth<TILE, false, true>(depth, a, b, pool_tiles, order, num_groups, group_tiles, sink, stream)
+             : launch_depth<TILE, false, false>(depth, a, b, pool_tiles, order, num_groups, group_tiles, sink, stream);
+}
+
 }  // namespace
 }  // namespace pkv
 
-extern "C" int pkv_read_probe(const void* a, const void* b, int64_t pool_tiles, int32_t tile_bytes,
-                              const int32_t* order, int32_t num_groups, int32_t group_tiles, uint32_t* sink,
-                              void* stream) {
+extern "C" pkv_status pkv_read_probe(const void* a, const void* b, int64_t pool_tiles, int32_t tile_bytes,
+                              const int32_t* order, int32_t num_groups, int32_t group_tiles, int32_t depth,
+                              uint32_t* sink, void* stream) {
   const auto aligned = [](const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; };
   if (tile_bytes != 4096 && tile_bytes != 8192)
     return pkv::set_error(PKV_EUNSUPPORTED, "tile_bytes must be 4096 or 8192 (got " + std::to_string(tile_bytes) + ")");
@@ -135,12 +153,15 @@ extern "C" int pkv_read_probe(const void* a, const void* b, int64_t pool_tiles, 
   if (int64_t(num_groups) * group_tiles > (int64_t(1) << 40) || pool_tiles > (int64_t(1) << 40) / tile_bytes)
     return pkv::set_error(PKV_EINVAL, "probe sizes out of range");
   if (!a || !sink) return pkv::set_error(PKV_EINVAL, "null pool a or sink");
+  if (depth < 2 || depth > (b ? 3 : 4))
+    return pkv::set_error(PKV_EUNSUPPORTED, "depth must be 2 or 3 with two pools, 2 to 4 with one (got " +
+                                                std::to_string(depth) + ")");
   if (!aligned(a, 16) || (b && !aligned(b, 16)) || (order && !aligned(order, 4)) || !aligned(sink, 4))
     return pkv::set_error(PKV_EINVAL, "pools must be 16-byte aligned, order and sink 4-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e =
-      tile_bytes == 4096 ? pkv::launch_tile<4096>(a, b, pool_tiles, order, num_groups, group_tiles, sink, st)
-                         : pkv::launch_tile<8192>(a, b, pool_tiles, order, num_groups, group_tiles, sink, st);
+      tile_bytes == 4096 ? pkv::launch_tile<4096>(depth, a, b, pool_tiles, order, num_groups, group_tiles, sink, st)
+                         : pkv::launch_tile<8192>(depth, a, b, pool_tiles, order, num_groups, group_tiles, sink, st);
   if (e != hipSuccess) return pkv::set_error(PKV_EHIP, std::string("pkv_read_probe launch: ") + hipGetErrorString(e));
   return pkv::set_error(PKV_OK, "");
 }

@@ -150,16 +150,6 @@ def pin_storage_upcast(o):
     assert o.to_float64(np.array([x]), "f32")[0] == float(x)
 
 
-def pin_round_to_storage(o):
-    g = golden("storage_bits.json")
-    for v, h in g["bf16_round_nearest_even"]:
-        got = o.round_to_storage(np.array([v]), "bf16")[0]
-        assert got == bf16_value(int(h, 16)), (v, got, h)
-    assert o.round_to_storage(np.array([1.0 + 2.0 ** -11]), "f16")[0] == 1.0          # tie -> even
-    assert o.round_to_storage(np.array([1.0 + 3 * 2.0 ** -11]), "f16")[0] == 1.0 + 2.0 ** -9
-    assert o.round_to_storage(np.array([1.0 + 2.0 ** -30]), "f32")[0] == 1.0
-
-
 def pin_slot_example(o):
     g = golden("slot_example.json")
     bs, blk = g["block_size"], g["block"]
@@ -480,7 +470,7 @@ def pin_prefill_prefix_chunks(o):
     assert np.max(np.abs(dec - full[[49, 82]])) <= 1e-12
 
 
-PINS = [pin_block_counts, pin_storage_upcast, pin_round_to_storage, pin_slot_example,
+PINS = [pin_block_counts, pin_storage_upcast, pin_slot_example,
         pin_write_then_read, pin_write_bitwise, pin_brute_force, pin_pages_tables,
         pin_permutation_invariance, pin_poison_invariance, pin_closed_forms,
         pin_split_equals_single, pin_prefix_sharing, pin_newest_token_slots, pin_prefill_brute_force,

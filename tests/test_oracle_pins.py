@@ -88,13 +88,6 @@ def _state_no_scale(q, K, V, scale):
     return O.__dict__["_orig_partition_state"](q, K, V, 1.0)
 
 
-def _round_truncate(x, dtype):
-    if dtype == "bf16":
-        u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32) >> 16
-        return O.to_float64(u.astype(np.uint16), "bf16")
-    return O.__dict__["_orig_round_to_storage"](x, dtype)
-
-
 def _decode_skip_last(q, k_cache, v_cache, block_tables, context_lens, scale, block_size, dtype, seqs=None):
     B = np.asarray(q).shape[0]
     return O.__dict__["_orig_decode"](q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
@@ -187,7 +180,6 @@ MUTANTS = {
     "merge forgets the LSE weights": ("lse_merge", _merge_unweighted),
     "merge weights with the wrong sign": ("lse_merge", _merge_wrong_sign),
     "partition state drops the scale": ("partition_state", _state_no_scale),
-    "bf16 rounding truncates": ("round_to_storage", _round_truncate),
     "decode skips the last sequence": ("decode", _decode_skip_last),
     "decode reads one token too few": ("decode", _decode_short_context),
     "write drops a token": ("kv_write", _write_skips_token0),

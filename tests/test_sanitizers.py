@@ -1,0 +1,38 @@
+"""The library's host code (argument validation, the block pool, the batch planner) under AddressSanitizer
+and UndefinedBehaviorSanitizer: a build with both on its host pass runs the ABI and block-pool tests in a
+child process with the sanitizer runtime preloaded; any report ends that run with a failure.  CPU only: the
+tests it runs make no GPU call."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from paged_kv_cache_383_amd import build as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def san_lib():
+    b.ensure_built()
+    return b.build_host_sanitized()
+
+
+def test_sanitized_build_is_instrumented(san_lib):
+    out = subprocess.run(["nm", "-D", san_lib], capture_output=True, text=True, check=True).stdout
+    assert "__asan_report_" in out and "__ubsan_handle_" in out
+
+
+def test_host_paths_clean_under_asan_and_ubsan(san_lib):
+    env = dict(os.environ, LD_PRELOAD=b.asan_runtime(), PKV_LIBRARY=san_lib,
+               ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:abort_on_error=0",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1",
+               HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1", CUDA_VISIBLE_DEVICES="-1")
+    res = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", "-m", "not gpu",
+                          "tests/test_abi.py", "tests/test_block_pool.py"],
+                         cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
+    tail = (res.stdout[-4000:] + "\n" + res.stderr[-4000:])
+    assert res.returncode == 0, tail
+    assert "AddressSanitizer" not in tail and "runtime error" not in tail, tail
+    assert " passed" in res.stdout, tail
