@@ -281,8 +281,9 @@ def read_ceiling(meta, sets, partition, reps=20):
     """HBM read ceilings on this GPU from the library's read probe (pkv_read_probe: the decode kernel's loads
     and wave layout, with no arithmetic), over the benchmark's own rotating K/V pools:
       decode_pattern   the decode's tiles in the decode's order: one work-group per (sequence, partition, head)
-                       with the head fastest, entries block_tables[s, j] * H + h of the partition's blocks, a
-                       ring of 2 stages (the decode kernel's own depth): the decode's gather without arithmetic;
+                       with the head fastest, entries block_tables[s, j] * H + h of the partition's blocks (each
+                       group stopping at its row's block count), a ring of 2 stages (the decode kernel's own
+                       depth): the decode's gather without arithmetic;
       random_tiles     every (block, head) tile of both pools once, in a random order, 128 per work-group;
       sequential       both pools streamed from start to end, 128 tiles per work-group;
       sequential_one_pool  the K pool alone, streamed, 4-stage ring;
@@ -306,7 +307,10 @@ def read_ceiling(meta, sets, partition, reps=20):
     h = torch.arange(H, device=dev, dtype=torch.int64).view(1, 1, H, 1)
     order_dec = torch.where(padded >= 0, padded * H + h, torch.full_like(padded * H + h, -1))
     order_dec = order_dec.reshape(B * P * H, pb).to(torch.int32).contiguous()
-    n_dec = int((tab >= 0).sum().item()) * H
+    nblk = (tab >= 0).sum(dim=1)                                  # each row's block count
+    p_first = torch.arange(P, device=dev, dtype=torch.int64).view(1, P, 1) * pb
+    len_dec = (nblk.view(B, 1, 1) - p_first).clamp(0, pb).expand(B, P, H).reshape(-1).to(torch.int32).contiguous()
+    n_dec = int(nblk.sum().item()) * H
     g = torch.Generator(device=dev)
     g.manual_seed(383383)
     group = 128
@@ -316,9 +320,9 @@ def read_ceiling(meta, sets, partition, reps=20):
     sink = torch.empty(8 * max(B * P * H, n_groups), dtype=torch.int32, device=dev)
     R = len(sets)
 
-    def timed(order, group_tiles, depth, two=True):
+    def timed(order, group_tiles, depth, two=True, group_len=None):
         run = lambda i: pkv.read_probe(sets[i % R].k_cache, sets[i % R].v_cache if two else None, tile, order,
-                                       group_tiles, sink, depth=depth)
+                                       group_tiles, sink, depth=depth, group_len=group_len)
         for i in range(3):
             run(i)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -330,7 +334,7 @@ def read_ceiling(meta, sets, partition, reps=20):
         return e0.elapsed_time(e1) * 1e3 / reps
 
     both = 2 * pool_tiles * tile
-    runs = {"decode_pattern": (timed(order_dec, pb, 2), 2 * n_dec * tile)}
+    runs = {"decode_pattern": (timed(order_dec, pb, 2, group_len=len_dec), 2 * n_dec * tile)}
     for d in (2, 3):
         runs[f"random_tiles_depth{d}"] = (timed(order_rand, group, d), both)
         runs[f"sequential_depth{d}"] = (timed(None, group, d), both)
@@ -604,7 +608,10 @@ def prefill(args):
 
     import paged_kv_cache_383_amd as pkv
     import workloads as W
+    import dataclasses
     cfg = W.PrefillConfig()
+    if args.prefill_dtype != cfg.dtype:
+        cfg = dataclasses.replace(cfg, dtype=args.prefill_dtype, name=cfg.name.rsplit("_", 1)[0] + "_" + args.prefill_dtype)
     dev = torch.device("cuda:0")
     H, D, bs = cfg.num_heads, cfg.head_dim, cfg.block_size
     es = elem_bytes(cfg.dtype)
@@ -665,7 +672,8 @@ def prefill(args):
                    "flops_per_step": flops, "write_bytes_per_step": write_b},
         "tokens_heads_per_s": round(T * H / step_s, 1),
         "kernels_us": {"paged_attention_prefill": round(pre_us, 2)},
-        "roofline": {"kernel": "paged_attention_prefill (prefill32_kernel: 32x32x16 MFMA tiles)", "bound": "mfma",
+        "roofline": {"kernel": ("paged_attention_prefill (prefill_kernel: 16x16x4 fp32 MFMA tiles)" if cfg.dtype == "f32"
+                               else "paged_attention_prefill (prefill32_kernel: 32x32x16 MFMA tiles)"), "bound": "mfma",
                      "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": None,
                      "algorithmic_flops_per_launch": flops, "mean_launch_us": round(pre_us, 2)},
@@ -701,6 +709,8 @@ def main():
     ap.add_argument("--two-call-step", action="store_true",
                     help="time the decode step as paged_kv_write + paged_attention_decode instead of the fused "
                          "paged_attention_decode_step")
+    ap.add_argument("--prefill-dtype", choices=["bf16", "f16", "f32"], default="bf16",
+                    help="element type of --workload prefill (the fp32 kernel is measured against the fp32 MFMA peak)")
     ap.add_argument("--copy-calibration", type=int, default=None, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()

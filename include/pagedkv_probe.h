@@ -36,6 +36,9 @@ extern "C" {
  *                 or NULL for 0, 1, 2, ... (a sequential stream of num_groups *
  *                 group_tiles tiles).  An entry outside [0, pool_tiles) is
  *                 skipped without a memory access (use -1 to pad).
+ *   group_len     int32 [num_groups] or NULL: group g reads only its first
+ *                 group_len[g] entries (clamped to [0, group_tiles]), as a decode
+ *                 work-group stops at its row's length; NULL = all of them
  *   num_groups    work-groups; group g reads entries g*group_tiles ..
  *                 (g+1)*group_tiles - 1 of the order
  *   group_tiles   entries per work-group (>= 1)
@@ -51,12 +54,13 @@ extern "C" {
  * depth for 16-bit tiles; deeper rings show what more loads in flight give.  With
  * the decode's own tile order (group = (sequence, head) row, entries =
  * block_tables[s, j] * num_heads + h, padded with -1) this is the decode's
- * gather with the arithmetic removed; with a random permutation it is a
+ * gather with the arithmetic removed (with group_len = each row's block count); with a random permutation it is a
  * random-tile read; with order NULL a sequential stream.
  * Bytes read per call = (1 or 2 pools) * tile_bytes * number of valid entries.
  */
 pkv_status pkv_read_probe(const void* a, const void* b, int64_t pool_tiles, int32_t tile_bytes, const int32_t* order,
-                   int32_t num_groups, int32_t group_tiles, int32_t depth, uint32_t* sink, void* stream);
+                          const int32_t* group_len, int32_t num_groups, int32_t group_tiles, int32_t depth,
+                          uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -93,7 +93,7 @@ def lib() -> ctypes.CDLL:
             "pkv_batch_set_row": ([vp, i32, i64], ctypes.c_int),
             "pkv_batch_plan_step": ([vp, i32, vp, i64, vp, vp, vp, i64, vp], ctypes.c_int),
             "paged_kv_prepare_step": ([vp, i32, vp, i32, vp, i64, vp, vp, i32, i64, vp], ctypes.c_int),
-            "pkv_read_probe": ([vp, vp, i64, i32, vp, i32, i32, i32, vp, vp], ctypes.c_int),
+            "pkv_read_probe": ([vp, vp, i64, i32, vp, vp, i32, i32, i32, vp, vp], ctypes.c_int),
             "paged_attention_decode_step_noalloc": ([vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i64,
                                                      ctypes.c_float, i32, vp, i32, vp], ctypes.c_int),
         }
@@ -292,10 +292,12 @@ def paged_attention_decode_step_noalloc(q, k_new, v_new, k_cache, v_cache, block
 NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
-def read_probe(a, b, tile_bytes: int, order, group_tiles: int, sink, num_groups=None, depth: int = 2):
+def read_probe(a, b, tile_bytes: int, order, group_tiles: int, sink, num_groups=None, depth: int = 2,
+               group_len=None):
     """Diagnostic HBM read (include/pagedkv_probe.h): tiles of ``tile_bytes`` of pools ``a`` and ``b`` (b may be
-    None) in the order of the int32 tensor ``order`` (None: sequential), ``group_tiles`` entries per work-group,
-    a ring of ``depth`` stages per wave; ``sink`` int32 receives one word per wave."""
+    None) in the order of the int32 tensor ``order`` (None: sequential), ``group_tiles`` entries per work-group
+    (of which group g reads the first ``group_len[g]`` when given), a ring of ``depth`` stages per wave;
+    ``sink`` int32 receives one word per wave."""
     import torch
     _device_tensor("a", a)
     if b is not None:
@@ -315,9 +317,14 @@ def read_probe(a, b, tile_bytes: int, order, group_tiles: int, sink, num_groups=
     _device_tensor("sink", sink, torch.int32)
     if sink.numel() < 8 * groups:
         raise ValueError("sink needs 8 words per work-group")
+    if group_len is not None:
+        _device_tensor("group_len", group_len, torch.int32, 1)
+        if group_len.numel() < groups:
+            raise ValueError("group_len needs one entry per work-group")
     _check(_launch(a.device, lib().pkv_read_probe, a.data_ptr(), None if b is None else b.data_ptr(), pool_tiles,
-                   int(tile_bytes), None if order is None else order.data_ptr(), int(groups), int(group_tiles),
-                   int(depth), sink.data_ptr()))
+                   int(tile_bytes), None if order is None else order.data_ptr(),
+                   None if group_len is None else group_len.data_ptr(), int(groups), int(group_tiles), int(depth),
+                   sink.data_ptr()))
     return groups
 
 

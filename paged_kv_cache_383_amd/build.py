@@ -92,26 +92,25 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
-SAN_LIB_PATH = os.path.join(LIB_DIR, "libpagedkv_hostsan.so")
+SAN_LIB_PATH = os.path.join(LIB_DIR, "libpagedkv_hostsan.so")      # default output of build_host_sanitized
 
 
-def build_host_sanitized() -> str:
+def build_host_sanitized(out_path: str = SAN_LIB_PATH) -> str:
     """The same library with AddressSanitizer and UndefinedBehaviorSanitizer on its host code only (every
     -fsanitize flag goes to the host pass; the gfx950 code is built as usual).  For CPU tests of the host
     paths: argument validation, the block pool and the batch planner.  Load it with the sanitizer runtime
     preloaded (asan_runtime()) and PKV_LIBRARY pointing at it."""
-    os.makedirs(LIB_DIR, exist_ok=True)
     host_san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-shared-libsan",
                 "-Xarch_host", "-fno-omit-frame-pointer"]
     flags = [f if f != "-O3" else "-O1" for f in compile_flags()] + ["-g"] + host_san
-    cmd = [hipcc(), *flags, "-shared", *[os.path.join(CSRC, s) for s in SOURCES], "-o", SAN_LIB_PATH + ".tmp"]
+    cmd = [hipcc(), *flags, "-shared", *[os.path.join(CSRC, s) for s in SOURCES], "-o", out_path + ".tmp"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     _report(res.stdout + res.stderr)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    os.replace(SAN_LIB_PATH + ".tmp", SAN_LIB_PATH)
-    return SAN_LIB_PATH
+    os.replace(out_path + ".tmp", out_path)
+    return out_path
 
 
 def asan_runtime() -> str:

@@ -36,20 +36,23 @@ template <int TILE, bool TWO, bool ORDERED, int DEPTH>
 __global__ __launch_bounds__(64 * kWaves) void read_probe_kernel(const char* __restrict__ a,
                                                                  const char* __restrict__ b, int64_t pool_tiles,
                                                                  const int32_t* __restrict__ order,
+                                                                 const int32_t* __restrict__ group_len,
                                                                  int32_t group_tiles, uint32_t* __restrict__ sink) {
   constexpr int kTps = kStageBytes / TILE;      // tiles per stage
   constexpr int kLoadsPerTile = TILE / 1024;    // wave-wide 1 KiB loads per tile
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t e0 = int64_t(blockIdx.x) * group_tiles;
-  const int units = (group_tiles + kTps - 1) / kTps;
+  // Entries this group reads: its first group_len[g] (clamped to [0, group_tiles]), or all of them.
+  const int n_entries = group_len ? min(max(group_len[blockIdx.x], 0), group_tiles) : group_tiles;
+  const int units = (n_entries + kTps - 1) / kTps;
   const int n_my = units > wave ? (units - wave + kWaves - 1) / kWaves : 0;
 
   // Tile index of entry u of this wave's stage i, or -1 (past the group, or an invalid entry).  Selects
   // only, no branch: the loop body stays one basic block.
   auto tile_at = [&](int i, int u) -> int64_t {
     const int k = (wave + kWaves * i) * kTps + u;
-    const bool live = i < n_my && k < group_tiles;
+    const bool live = i < n_my && k < n_entries;
     const int64_t e = e0 + (live ? k : 0);
     int64_t id = e;
     if constexpr (ORDERED) id = __builtin_amdgcn_readfirstlane(order[e]);
@@ -115,36 +118,41 @@ __global__ __launch_bounds__(64 * kWaves) void read_probe_kernel(const char* __r
 
 template <int TILE, bool TWO, bool ORDERED>
 hipError_t launch_depth(int depth, const void* a, const void* b, int64_t pool_tiles, const int32_t* order,
-                        int32_t num_groups, int32_t group_tiles, uint32_t* sink, hipStream_t stream) {
+                        const int32_t* group_len, int32_t num_groups, int32_t group_tiles, uint32_t* sink,
+                        hipStream_t stream) {
   // Two pools stop at depth 3: a fourth pair of stage buffers does not fit the registers.
-  void (*kernel)(const char*, const char*, int64_t, const int32_t*, int32_t, uint32_t*) =
+  void (*kernel)(const char*, const char*, int64_t, const int32_t*, const int32_t*, int32_t, uint32_t*) =
       depth == 2 ? read_probe_kernel<TILE, TWO, ORDERED, 2> : read_probe_kernel<TILE, TWO, ORDERED, 3>;
   if constexpr (!TWO) {
     if (depth == 4) kernel = read_probe_kernel<TILE, TWO, ORDERED, 4>;
   }
   hipLaunchKernelGGL(kernel, dim3(unsigned(num_groups)), dim3(64 * kWaves), 0, stream,
-                     static_cast<const char*>(a), static_cast<const char*>(b), pool_tiles, order, group_tiles, sink);
+                     static_cast<const char*>(a), static_cast<const char*>(b), pool_tiles, order, group_len,
+                     group_tiles, sink);
   return hipGetLastError();
 }
 
 template <int TILE>
 hipError_t launch_tile(int depth, const void* a, const void* b, int64_t pool_tiles, const int32_t* order,
-                       int32_t num_groups, int32_t group_tiles, uint32_t* sink, hipStream_t stream) {
+                       const int32_t* group_len, int32_t num_groups, int32_t group_tiles, uint32_t* sink,
+                       hipStream_t stream) {
   if (b != nullptr)
-    return order != nullptr
-               ? launch_depth<TILE, true, true>(depth, a, b, pool_tiles, order, num_groups, group_tiles, sink, stream)
-               : launch_depth<TILE, true, false>(depth, a, b, pool_tiles, order, num_groups, group_tiles, sink, stream);
-  return order != nullptr
-             ? launch_depth<TILE, false, true>(depth, a, b, pool_tiles, order, num_groups, group_tiles, sink, stream)
-             : launch_depth<TILE, false, false>(depth, a, b, pool_tiles, order, num_groups, group_tiles, sink, stream);
+    return order != nullptr ? launch_depth<TILE, true, true>(depth, a, b, pool_tiles, order, group_len, num_groups,
+                                                              group_tiles, sink, stream)
+                            : launch_depth<TILE, true, false>(depth, a, b, pool_tiles, order, group_len, num_groups,
+                                                               group_tiles, sink, stream);
+  return order != nullptr ? launch_depth<TILE, false, true>(depth, a, b, pool_tiles, order, group_len, num_groups,
+                                                             group_tiles, sink, stream)
+                          : launch_depth<TILE, false, false>(depth, a, b, pool_tiles, order, group_len, num_groups,
+                                                              group_tiles, sink, stream);
 }
 
 }  // namespace
 }  // namespace pkv
 
 extern "C" pkv_status pkv_read_probe(const void* a, const void* b, int64_t pool_tiles, int32_t tile_bytes,
-                              const int32_t* order, int32_t num_groups, int32_t group_tiles, int32_t depth,
-                              uint32_t* sink, void* stream) {
+                                     const int32_t* order, const int32_t* group_len, int32_t num_groups,
+                                     int32_t group_tiles, int32_t depth, uint32_t* sink, void* stream) {
   const auto aligned = [](const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; };
   if (tile_bytes != 4096 && tile_bytes != 8192)
     return pkv::set_error(PKV_EUNSUPPORTED, "tile_bytes must be 4096 or 8192 (got " + std::to_string(tile_bytes) + ")");
@@ -156,12 +164,14 @@ extern "C" pkv_status pkv_read_probe(const void* a, const void* b, int64_t pool_
   if (depth < 2 || depth > (b ? 3 : 4))
     return pkv::set_error(PKV_EUNSUPPORTED, "depth must be 2 or 3 with two pools, 2 to 4 with one (got " +
                                                 std::to_string(depth) + ")");
-  if (!aligned(a, 16) || (b && !aligned(b, 16)) || (order && !aligned(order, 4)) || !aligned(sink, 4))
-    return pkv::set_error(PKV_EINVAL, "pools must be 16-byte aligned, order and sink 4-byte aligned");
+  if (!aligned(a, 16) || (b && !aligned(b, 16)) || (order && !aligned(order, 4)) || (group_len && !aligned(group_len, 4)) ||
+      !aligned(sink, 4))
+    return pkv::set_error(PKV_EINVAL, "pools must be 16-byte aligned, order, group_len and sink 4-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e =
-      tile_bytes == 4096 ? pkv::launch_tile<4096>(depth, a, b, pool_tiles, order, num_groups, group_tiles, sink, st)
-                         : pkv::launch_tile<8192>(depth, a, b, pool_tiles, order, num_groups, group_tiles, sink, st);
+      tile_bytes == 4096
+          ? pkv::launch_tile<4096>(depth, a, b, pool_tiles, order, group_len, num_groups, group_tiles, sink, st)
+          : pkv::launch_tile<8192>(depth, a, b, pool_tiles, order, group_len, num_groups, group_tiles, sink, st);
   if (e != hipSuccess) return pkv::set_error(PKV_EHIP, std::string("pkv_read_probe launch: ") + hipGetErrorString(e));
   return pkv::set_error(PKV_OK, "");
 }

@@ -86,11 +86,12 @@ def wr(**kw):
     a.update(kw)
     return lib.paged_kv_write(a["k"], a["v"], a["s"], a["T"], a["kc"], a["vc"], a["NB"], a["H"], a["D"],
                               a["bs"], a["dt"], None)
-lib.pkv_read_probe.argtypes = [vp, vp, i64, i32, vp, i32, i32, i32, vp, vp]
+lib.pkv_read_probe.argtypes = [vp, vp, i64, i32, vp, vp, i32, i32, i32, vp, vp]
 def rp(**kw):
-    a = dict(a=F, b=F, n=1024, tb=4096, o=F, g=8, gt=128, depth=2, sink=F)
+    a = dict(a=F, b=F, n=1024, tb=4096, o=F, gl=None, g=8, gt=128, depth=2, sink=F)
     a.update(kw)
-    return lib.pkv_read_probe(a["a"], a["b"], a["n"], a["tb"], a["o"], a["g"], a["gt"], a["depth"], a["sink"], None)
+    return lib.pkv_read_probe(a["a"], a["b"], a["n"], a["tb"], a["o"], a["gl"], a["g"], a["gt"], a["depth"],
+                              a["sink"], None)
 ws = lib.paged_attention_workspace_bytes(64, 40, 128, 128, 16, 512)
 cases = [
   ("dec_dtype", lambda: dec(dt=7), 2), ("dec_head_dim", lambda: dec(D=96), 2),
@@ -119,7 +120,7 @@ cases = [
   ("rp_groups", lambda: rp(g=0), 1), ("rp_group_tiles", lambda: rp(gt=0), 1), ("rp_pool", lambda: rp(n=0), 1),
   ("rp_misaligned_b", lambda: rp(b=F + 8), 1), ("rp_misaligned_order", lambda: rp(o=F + 2), 1),
   ("rp_depth_two_pools", lambda: rp(depth=4), 2), ("rp_depth_low", lambda: rp(depth=1, b=None), 2),
-  ("rp_depth_high", lambda: rp(depth=5, b=None), 2),
+  ("rp_depth_high", lambda: rp(depth=5, b=None), 2), ("rp_misaligned_len", lambda: rp(gl=F + 1), 1),
 ]
 for name, call, want in cases:
     got = call()

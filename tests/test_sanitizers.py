@@ -14,9 +14,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 @pytest.fixture(scope="module")
-def san_lib():
+def san_lib(tmp_path_factory):
     b.ensure_built()
-    return b.build_host_sanitized()
+    return b.build_host_sanitized(str(tmp_path_factory.mktemp("hostsan") / "libpagedkv_hostsan.so"))
 
 
 def test_sanitized_build_is_instrumented(san_lib):
