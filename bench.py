@@ -659,10 +659,22 @@ def prefill(args):
     b.record()
     torch.cuda.synchronize()
     pre_us = a.elapsed_time(b) * 1e3 / args.steps
+    # isolated launches: each bracketed by its own event pair with the GPU idle before it (no overlap with a
+    # neighbouring launch), the start-to-end duration a kernel trace records
+    iso = []
+    for _ in range(min(args.steps, 20)):
+        torch.cuda.synchronize()
+        a.record()
+        pkv.paged_attention_prefill(q, kc, vc, t_tables, t_qs, t_ctx, cfg.scale, maxq, out=out)
+        b.record()
+        torch.cuda.synchronize()
+        iso.append(a.elapsed_time(b) * 1e3)
+    iso_us = sum(iso) / len(iso)
     tflops = flops / pre_us / 1e6
     peak = PEAK_MFMA_TFLOPS[cfg.dtype]
     log(f"{cfg.name}: {T} tokens, {pairs} causal pairs; step {step_s * 1e6:.1f} us; prefill kernel {pre_us:.1f} us "
-        f"= {tflops:.1f} TFLOP/s ({tflops / peak:.1%} of {peak:.0f})")
+        f"= {tflops:.1f} TFLOP/s ({tflops / peak:.1%} of {peak:.0f}); isolated launches {iso_us:.1f} us "
+        f"({flops / iso_us / 1e6 / peak:.1%})")
     rec = {
         "metric": METRIC, "value": round(T / step_s, 1), "unit": "prompt tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 5),
@@ -671,7 +683,7 @@ def prefill(args):
                    "block_size": bs, "step": "paged_kv_write(prompt K/V) + paged_attention_prefill",
                    "flops_per_step": flops, "write_bytes_per_step": write_b},
         "tokens_heads_per_s": round(T * H / step_s, 1),
-        "kernels_us": {"paged_attention_prefill": round(pre_us, 2)},
+        "kernels_us": {"paged_attention_prefill": round(pre_us, 2), "paged_attention_prefill_isolated": round(iso_us, 2)},
         "roofline": {"kernel": ("paged_attention_prefill (prefill_kernel: 16x16x4 fp32 MFMA tiles)" if cfg.dtype == "f32"
                                else "paged_attention_prefill (prefill32_kernel: 32x32x16 MFMA tiles)"), "bound": "mfma",
                      "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
@@ -706,6 +718,8 @@ def main():
                     help="split-context partition in tokens (0 = one pass); default: the library's choice")
     ap.add_argument("--rotate", type=int, default=None, help="independent input copies cycled over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-diagnostic", action="store_true",
+                    help="skip the read-probe ceilings and the PyTorch streaming figures (counter runs)")
     ap.add_argument("--two-call-step", action="store_true",
                     help="time the decode step as paged_kv_write + paged_attention_decode instead of the fused "
                          "paged_attention_decode_step")
@@ -851,11 +865,13 @@ def main():
         f"{graph_us:.1f} us), decode {decode_us:.1f} us, "
         f"write {write_us:.1f} us -> decode {achieved:.0f} GB/s = {achieved / PEAK_HBM_GBS:.1%} of peak")
 
-    stream_ref = torch_stream_reference()
-    log(f"plain PyTorch streaming on this GPU: {stream_ref}")
-    probe = read_ceiling(meta, sets, resolved)
-    probe["decode_call_frac_of_best"] = round(achieved / probe["best"]["GB_per_s"], 4)
-    log(f"read probe on this GPU: {probe}")
+    stream_ref = probe = None
+    if not args.no_diagnostic:
+        stream_ref = torch_stream_reference()
+        log(f"plain PyTorch streaming on this GPU: {stream_ref}")
+        probe = read_ceiling(meta, sets, resolved)
+        probe["decode_call_frac_of_best"] = round(achieved / probe["best"]["GB_per_s"], 4)
+        log(f"read probe on this GPU: {probe}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -911,7 +927,7 @@ def main():
             "algorithmic_bytes_per_launch": nbytes["decode"],
             "mean_launch_us": round(decode_us, 2),
         },
-        "diagnostic": {"read_probe": probe, "torch_streaming": stream_ref},
+        "diagnostic": None if args.no_diagnostic else {"read_probe": probe, "torch_streaming": stream_ref},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
