@@ -702,18 +702,82 @@ def prefill(args):
     print(json.dumps(rec), flush=True)
 
 
+SPLIT_SWEEP_SHAPES = [(1, 40, 32768), (2, 40, 16384), (1, 32, 8192), (4, 40, 32768)]   # (sequences, heads, context)
+
+
+def split_sweep(args):
+    """The decode call at few (sequence, head) rows, where the library splits contexts into partitions: the
+    library's automatic choice beside fixed partition sizes, at the LLaMA-2-13B head shape (D 128, 16-token
+    blocks, bf16, every sequence at the full context, blocks in a shuffled pool).  One JSON line."""
+    import torch
+
+    import paged_kv_cache_383_amd as pkv
+    import workloads as W
+    dev = torch.device("cuda:0")
+    bs, D = 16, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(383500)
+    rows = []
+    for B, H, L in SPLIT_SWEEP_SHAPES:
+        nb_seq = L // bs
+        NB = B * nb_seq
+        k, v = W.kv_pool(NB, H, bs, D, torch.bfloat16, dev)
+        W._randn_into(k, gen, 1.0, 1024)
+        W._randn_into(v, gen, 1.0, 1024)
+        tables = torch.randperm(NB, generator=gen, device=dev).to(torch.int32).view(B, nb_seq).contiguous()
+        lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+        q = torch.randn((B, H, D), generator=gen, device=dev).to(torch.bfloat16)
+        out = torch.empty_like(q)
+        nbytes = B * L * H * D * 2 * 2 + B * H * D * 2 * 2 + 4 * B * nb_seq + 4 * B
+        res = {}
+        # two rounds over the partition sizes; the first only warms the new pools, the second is reported
+        for part in [pkv.PARTITION_AUTO, 512, 1024, 2048, 4096] * 2:
+            ws = torch.empty(max(pkv.paged_attention_workspace_bytes(B, H, D, nb_seq, bs, part), 1), dtype=torch.uint8,
+                             device=dev)
+            run = lambda: pkv.paged_attention_decode(q, k, v, tables, lens, 1.0 / math.sqrt(D), out=out, workspace=ws,
+                                                     partition_size=part)
+            for _ in range(args.warmup):
+                run()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(args.steps):
+                run()
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / args.steps
+            res["auto" if part == pkv.PARTITION_AUTO else str(part)] = {"us": round(us, 2),
+                                                                       "GB_per_s": round(nbytes / us / 1e3, 1)}
+        auto = pkv.paged_attention_partition_size(B, H, nb_seq, bs, pkv.PARTITION_AUTO)
+        log(f"B={B} H={H} L={L}: automatic partition {auto} tokens; " +
+            " ".join(f"{k_}: {v_['us']} us" for k_, v_ in res.items()))
+        rows.append({"num_seqs": B, "num_heads": H, "context": L, "auto_partition": auto, "bytes": nbytes,
+                     "decode": res})
+        del k, v
+        torch.cuda.empty_cache()
+    first = rows[0]["decode"]["auto"]          # the line's value: the first shape at the automatic split
+    rec = {"metric": METRIC, "value": first["GB_per_s"], "unit": "GB/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(first["us"] / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "split_sweep_few_rows_h40_d128_bs16_bf16", "shapes": rows},
+           "cpu_baseline": None}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--workload", choices=["decode", "parallel_sampling", "continuous_batching", "prefill"],
+    ap.add_argument("--workload", choices=["decode", "parallel_sampling", "continuous_batching", "prefill",
+                                           "split_sweep"],
                     default="decode",
                     help="decode: one decode step of --config; parallel_sampling: a decode step over "
                          "prompts shared by parallel samples (copy-on-write copies + write + decode); "
                          "continuous_batching: a many-step decode loop with admissions and releases; "
-                         "prefill: prompt K/V writes + causal paged prefill attention (MFMA)")
+                         "prefill: prompt K/V writes + causal paged prefill attention (MFMA); "
+                         "split_sweep: the decode call at few rows, automatic split beside fixed partitions")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="split-context partition in tokens (0 = one pass); default: the library's choice")
     ap.add_argument("--rotate", type=int, default=None, help="independent input copies cycled over")
@@ -752,6 +816,9 @@ def main():
         return
     if args.workload == "prefill":
         prefill(args)
+        return
+    if args.workload == "split_sweep":
+        split_sweep(args)
         return
 
     dev = torch.device("cuda:0")

@@ -107,10 +107,10 @@ pkv_status paged_kv_write(const void* k, const void* v, const int64_t* slot_mapp
  * paged_attention_decode uses for these sizes: partition_size itself, or for
  * PKV_PARTITION_AUTO the library's choice.  The automatic choice is 0 (no
  * split) when num_seqs * num_heads >= 1024, since the grid then already holds
- * several work-groups per compute unit; otherwise the smallest multiple of 512
+ * several work-groups per compute unit; otherwise the smallest multiple of 1024
  * tokens that cuts the table's capacity (max_blocks_per_seq * block_size) into
- * about 4096 / (num_seqs * num_heads) partitions, or 0 if that is the whole
- * capacity.  Results do not depend on the split beyond fp32 rounding.
+ * at most ceil(1280 / (num_seqs * num_heads)) partitions, or 0 if that is the
+ * whole capacity.  Results do not depend on the split beyond fp32 rounding.
  */
 int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
                                        int32_t block_size, int32_t partition_size);

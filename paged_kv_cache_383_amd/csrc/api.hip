@@ -85,10 +85,14 @@ int32_t part_blocks_for(int32_t max_blocks, int32_t block_size, int32_t partitio
 // already holds several work-groups per compute unit, and one pass per row
 // is fastest (no partials, no merge).  With fewer rows, contexts are cut into
 // partitions, multiples of kAutoGrain tokens, so that about
-// kAutoTargetGroups work-groups cover the longest possible context.
+// kAutoTargetGroups work-groups (about 5 per compute unit) cover the longest
+// possible context.  The grain keeps at least 4 stages per wave in a 16-token
+// block partition: with 512-token partitions each wave has 2, and the
+// work-group's fixed costs (merge, partial state, the reduce) dominate (one
+// sequence x 40 heads x 32k tokens: 126 us at 512, 109 us at 1024).
 constexpr int64_t kAutoMinRows = 1024;
-constexpr int64_t kAutoTargetGroups = 2560;   // 32k-token rows: 4096-token partitions (823 us vs 841 at 2560 tokens)
-constexpr int64_t kAutoGrain = 512;
+constexpr int64_t kAutoTargetGroups = 1280;
+constexpr int64_t kAutoGrain = 1024;
 
 int32_t resolve_partition(int32_t num_seqs, int32_t num_heads, int32_t max_blocks, int32_t block_size,
                           int32_t partition_size) {

@@ -143,10 +143,10 @@ def test_validation_returns_status_before_any_launch(libpath):
     assert res.returncode == 0, res.stderr
     lines = res.stdout.strip().splitlines()
     auto = [int(x) for x in lines[-2].split()[1:]]
-    # >= 1024 rows: one pass; 320 rows of a 32768-token table: ceil(2560 / 320) = 8 partitions of
-    # 32768 / 8 = 4096 tokens; a tiny table: no split; one row: 4096 / 2560 -> 26 -> 512 tokens
-    assert auto[:6] == [0, 4096, 0, 512, 512, 0]
-    n_auto = 8 * 40 * 8
+    # >= 1024 rows: one pass; 320 rows of a 32768-token table: ceil(1280 / 320) = 4 partitions of
+    # 32768 / 4 = 8192 tokens; a tiny table: no split; one row: 65536 / 1280 -> 52 -> 1024 tokens (the grain)
+    assert auto[:6] == [0, 8192, 0, 1024, 512, 0]
+    n_auto = 8 * 40 * 4
     assert auto[6] == 2 * ((n_auto * 4 + 255) // 256 * 256) + n_auto * 128 * 4
     for line in lines[:-2]:
         name, got, want, _ = line.split(" ", 3)
