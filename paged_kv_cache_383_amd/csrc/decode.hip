@@ -461,16 +461,24 @@ __global__ __launch_bounds__(64 * WAVES) void decode_partition_kernel(
 }
 
 // Merge the partitions of every (sequence, head) whose context spans more
-// than one: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+// than one: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p, M = max_p
+// m_p.  Four waves per (head, sequence): wave w folds partitions w, w + 4, ...
+// into a running (max, numerator, denominator) with each lane holding D / 64
+// dims, so up to four partitions' loads are in flight per row at once; the
+// four states are then merged through LDS.  A wave that got no partition
+// keeps the empty state, whose weight 2^(kEmptyMax - M) is 0.
+constexpr int kReduceWaves = 4;
 template <int DT, int D>
-__global__ __launch_bounds__(D) void lse_reduce_kernel(
+__global__ __launch_bounds__(64 * kReduceWaves) void lse_reduce_kernel(
     const int32_t* __restrict__ context_lens, const float* __restrict__ ws_m,
     const float* __restrict__ ws_l, const float* __restrict__ ws_acc, void* __restrict__ out,
     int32_t max_blocks, int32_t block_size, int32_t part_blocks, int32_t partitions) {
+  constexpr int kDpl = D / 64;                            // dims per lane
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int H = gridDim.x;
-  const int d = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int32_t L = context_lens[s];
   if (L <= 0 || !context_ok(L, max_blocks * block_size)) return;
   const int nb = (L + block_size - 1) / block_size;
@@ -478,15 +486,47 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(
   if (parts <= 1) return;
   const int64_t row = int64_t(s) * H + h;
   const int64_t base = row * partitions;
-  float M = kEmptyMax;
-  for (int p = 0; p < parts; ++p) M = fmaxf(M, ws_m[base + p]);
-  float num = 0.f, den = 0.f;
-  for (int p = 0; p < parts; ++p) {
-    const float w = exp2_fast(ws_m[base + p] - M);
-    num = __builtin_fmaf(w, ws_acc[(base + p) * D + d], num);
-    den = __builtin_fmaf(w, ws_l[base + p], den);
+  float m = kEmptyMax, den = 0.f, num[kDpl];
+#pragma unroll
+  for (int e = 0; e < kDpl; ++e) num[e] = 0.f;
+  for (int p = wave; p < parts; p += kReduceWaves) {
+    const float mp = ws_m[base + p];
+    const float lp = ws_l[base + p];
+    const float m_new = fmaxf(m, mp);
+    const float a = exp2_fast(m - m_new);
+    const float b = exp2_fast(mp - m_new);
+    den = __builtin_fmaf(den, a, lp * b);
+    const float* accp = ws_acc + (base + p) * D + lane * kDpl;
+#pragma unroll
+    for (int e = 0; e < kDpl; ++e) num[e] = __builtin_fmaf(num[e], a, accp[e] * b);
+    m = m_new;
   }
-  store_elem<DT>(out, row * D + d, num / den);
+  __shared__ float sm_m[kReduceWaves];
+  __shared__ float sm_den[kReduceWaves];
+  __shared__ float sm_num[kReduceWaves * D];
+  if (lane == 0) {
+    sm_m[wave] = m;
+    sm_den[wave] = den;
+  }
+#pragma unroll
+  for (int e = 0; e < kDpl; ++e) sm_num[wave * D + lane * kDpl + e] = num[e];
+  __syncthreads();
+  if (wave != 0) return;
+  float M = kEmptyMax;
+#pragma unroll
+  for (int w = 0; w < kReduceWaves; ++w) M = fmaxf(M, sm_m[w]);
+  float d = 0.f, n[kDpl];
+#pragma unroll
+  for (int e = 0; e < kDpl; ++e) n[e] = 0.f;
+#pragma unroll
+  for (int w = 0; w < kReduceWaves; ++w) {
+    const float f = exp2_fast(sm_m[w] - M);
+    d = __builtin_fmaf(f, sm_den[w], d);
+#pragma unroll
+    for (int e = 0; e < kDpl; ++e) n[e] = __builtin_fmaf(f, sm_num[w * D + lane * kDpl + e], n[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < kDpl; ++e) store_elem<DT>(out, row * D + lane * kDpl + e, n[e] / d);
 }
 
 template <int DT, int D, int BS>
@@ -505,7 +545,7 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.partitions <= 1) return e;
   hipLaunchKernelGGL((lse_reduce_kernel<DT, D>), dim3(unsigned(a.num_heads), unsigned(a.num_seqs)),
-                     dim3(D), 0, stream, a.context_lens, a.ws_m, a.ws_l, a.ws_acc, a.out,
+                     dim3(64 * kReduceWaves), 0, stream, a.context_lens, a.ws_m, a.ws_l, a.ws_acc, a.out,
                      a.max_blocks, BS, a.part_blocks, a.partitions);
   return hipGetLastError();
 }
