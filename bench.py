@@ -600,6 +600,39 @@ def continuous_batching(args):
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense matrix peaks, published
 
 
+def mfma_ceiling(dtype_name, reps=4):
+    """Matrix-core ceilings on this GPU from the library's probe (pkv_mfma_probe: the prefill kernel's product
+    instruction, v_mfma_f32_32x32x16, with nothing else to do), at 1, 2 and 3 waves per SIMD (the prefill kernel
+    runs 3), and at 3 waves with 4 vector additions per product.  Each: TFLOP/s over the launch (events, the last
+    of ``reps`` launches of about 1-3 ms) and the shader clock the waves recorded.  A diagnostic only."""
+    import torch
+
+    import paged_kv_cache_383_amd as pkv
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype_name]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = pkv.MFMA_PROBE_MAX_ITERS
+    out = {}
+    for waves, valu in ((1, 0), (2, 0), (3, 0), (3, 4)):
+        groups = cus * waves
+        sink = torch.empty(groups * 256, dtype=torch.float32, device="cuda:0")
+        clocks = torch.zeros(groups * 8, dtype=torch.int64, device="cuda:0")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(reps):
+            a.record()
+            pkv.mfma_probe(dt, groups, iters, sink, clocks, valu=valu)
+            b.record()
+            torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3
+        flops = groups * 4 * iters * 8 * 32 * 32 * 16 * 2
+        c = clocks.view(-1, 2).double()
+        ghz = float((c[:, 0] / c[:, 1]).median()) * 0.1
+        ok = bool((sink == float(2048 * iters + 8 * valu * iters)).all())
+        out[f"waves{waves}_valu{valu}"] = {"us": round(us, 1), "tflops": round(flops / us / 1e6, 1),
+                                            "clock_ghz": round(ghz, 3), "sums_exact": ok}
+    out["best_tflops"] = max(v["tflops"] for k, v in out.items() if k.endswith("valu0"))
+    return out
+
+
 def prefill(args):
     """Prefill of a batch of prompts: the prompts' K/V are written into the paged cache (paged_kv_write),
     then every prompt token attends causally over its sequence (paged_attention_prefill, MFMA)."""
@@ -691,6 +724,13 @@ def prefill(args):
                      "algorithmic_flops_per_launch": flops, "mean_launch_us": round(pre_us, 2)},
         "cpu_baseline": None,
     }
+    if not args.no_diagnostic and cfg.dtype in ("bf16", "f16"):
+        ceiling = mfma_ceiling(cfg.dtype)
+        ceiling["prefill_frac_of_best"] = round(tflops / ceiling["best_tflops"], 4)
+        rec["diagnostic"] = {"mfma_probe": ceiling}
+        log("mfma probe: " + "; ".join(f"{k} {v['tflops']} TFLOP/s at {v['clock_ghz']} GHz" for k, v in ceiling.items()
+                                       if isinstance(v, dict))
+            + f" -> prefill {tflops:.0f} TFLOP/s = {ceiling['prefill_frac_of_best']:.1%} of the best")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle's prefill on a sample of the same prompts ...")
         order_short = np.argsort(lens, kind="stable")           # shortest prompts first: more of them fit
@@ -783,7 +823,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=None, help="independent input copies cycled over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-diagnostic", action="store_true",
-                    help="skip the read-probe ceilings and the PyTorch streaming figures (counter runs)")
+                    help="skip the read-probe and matrix-core-probe ceilings and the PyTorch streaming figures (counter runs)")
     ap.add_argument("--two-call-step", action="store_true",
                     help="time the decode step as paged_kv_write + paged_attention_decode instead of the fused "
                          "paged_attention_decode_step")

@@ -1,6 +1,7 @@
 /*
- * pagedkv_probe.h -- diagnostic entry point of libpagedkv.so: an HBM read
- * ceiling for the decode kernel's access pattern.
+ * pagedkv_probe.h -- diagnostic entry points of libpagedkv.so: an HBM read
+ * ceiling for the decode kernel's access pattern, and a matrix-core ceiling
+ * for the prefill kernel's products.
  *
  * Decode reads the whole K/V cache once per step and is bound by memory
  * bandwidth ("vLLM KV cache and PagedAttention explained", Step 6: every
@@ -61,6 +62,34 @@ extern "C" {
 pkv_status pkv_read_probe(const void* a, const void* b, int64_t pool_tiles, int32_t tile_bytes, const int32_t* order,
                           const int32_t* group_len, int32_t num_groups, int32_t group_tiles, int32_t depth,
                           uint32_t* sink, void* stream);
+
+/*
+ * pkv_mfma_probe -- the matrix-core ceiling for the prefill kernel's products.
+ * Prefill is the one dense contraction of the path and is compute-bound
+ * ("vLLM KV cache and PagedAttention explained", Step 6); the published peak
+ * assumes the 2.4 GHz maximum clock, which a long run of dense products does
+ * not keep.  This runs the prefill kernel's product instruction with nothing
+ * else to do and reports what this GPU sustains.  Not part of the prefill.
+ *
+ *   dtype        PKV_BF16 or PKV_F16: v_mfma_f32_32x32x16 of that type
+ *   num_groups   work-groups of 4 wave64 (one per SIMD of a compute unit);
+ *                num_groups = k x the number of compute units gives k waves per SIMD
+ *   iters        loop iterations per wave, 8 products each into 4 independent
+ *                accumulators; 1 .. PKV_MFMA_PROBE_MAX_ITERS
+ *   valu         0, 4 or 8 vector additions after each product (the way a
+ *                softmax shares a SIMD with the products)
+ *   sink         float [num_groups * 256], written: every operand is 1, so lane
+ *                value = 2048 * iters + 8 * valu * iters, exactly
+ *   clocks       uint64 [num_groups * 4 * 2] or NULL: per wave (index
+ *                group * 4 + wave), the shader-clock cycles and the 100 MHz
+ *                reference-clock ticks between its first and last product;
+ *                cycles / ticks x 100 MHz is the shader clock over the run
+ *
+ * Products per call = num_groups * 4 * iters * 8, each 32 * 32 * 16 * 2 flops.
+ */
+#define PKV_MFMA_PROBE_MAX_ITERS 8000
+pkv_status pkv_mfma_probe(int32_t dtype, int32_t num_groups, int32_t iters, int32_t valu, float* sink,
+                          uint64_t* clocks, void* stream);
 
 #ifdef __cplusplus
 }

@@ -94,6 +94,7 @@ def lib() -> ctypes.CDLL:
             "pkv_batch_plan_step": ([vp, i32, vp, i64, vp, vp, vp, i64, vp], ctypes.c_int),
             "paged_kv_prepare_step": ([vp, i32, vp, i32, vp, i64, vp, vp, i32, i64, vp], ctypes.c_int),
             "pkv_read_probe": ([vp, vp, i64, i32, vp, vp, i32, i32, i32, vp, vp], ctypes.c_int),
+            "pkv_mfma_probe": ([i32, i32, i32, i32, vp, vp, vp], ctypes.c_int),
             "paged_attention_decode_step_noalloc": ([vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i64,
                                                      ctypes.c_float, i32, vp, i32, vp], ctypes.c_int),
         }
@@ -326,6 +327,29 @@ def read_probe(a, b, tile_bytes: int, order, group_tiles: int, sink, num_groups=
                    None if group_len is None else group_len.data_ptr(), int(groups), int(group_tiles), int(depth),
                    sink.data_ptr()))
     return groups
+
+
+MFMA_PROBE_MAX_ITERS = 8000
+
+
+def mfma_probe(dtype, num_groups: int, iters: int, sink, clocks=None, valu: int = 0):
+    """Diagnostic matrix-core run (include/pagedkv_probe.h): ``num_groups`` work-groups of 4 waves, each wave
+    ``iters`` x 8 products v_mfma_f32_32x32x16 of ``dtype`` (torch.bfloat16 or torch.float16) with ``valu``
+    vector additions after each; ``sink`` float32 [num_groups * 256] receives exact sums, ``clocks`` (int64
+    [num_groups * 8] or None) the shader-clock cycles and 100 MHz reference ticks of every wave."""
+    import torch
+    _device_tensor("sink", sink, torch.float32)
+    if sink.numel() < 256 * int(num_groups):
+        raise ValueError("sink needs 256 floats per work-group")
+    if clocks is not None:
+        _device_tensor("clocks", clocks, torch.int64)
+        if clocks.numel() < 8 * int(num_groups):
+            raise ValueError("clocks needs 8 words per work-group")
+    code = {torch.bfloat16: PKV_BF16, torch.float16: PKV_F16}.get(dtype)
+    if code is None:
+        raise TypeError(f"the probe runs bf16 or f16 products, not {dtype}")
+    _check(_launch(sink.device, lib().pkv_mfma_probe, code, int(num_groups), int(iters), int(valu),
+                   sink.data_ptr(), None if clocks is None else clocks.data_ptr()))
 
 
 def paged_attention_prefill(q, k_cache, v_cache, block_tables, query_start, context_lens, scale,

@@ -30,7 +30,7 @@ LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libpagedkv.so")
 STAMP_PATH = LIB_PATH + ".sha256"
 SOURCES = ["api.hip", "kv_write.hip", "decode.hip", "decode_noalloc.hip", "copy_blocks.hip", "step.hip",
-           "prefill.hip", "read_probe.hip", "block_pool.cpp"]
+           "prefill.hip", "read_probe.hip", "mfma_probe.hip", "block_pool.cpp"]
 ARCH = "gfx950"
 # The host pass's notice about the device-only feature above; nothing else is filtered.
 _HOST_FEATURE_NOTICE = "'-packed-fp32-ops' is not a recognized feature for this target"

@@ -506,11 +506,18 @@ __global__ __launch_bounds__(64 * kWaves32) __attribute__((amdgpu_waves_per_eu(3
   static_assert(kNl * kWaves32 * kRowsPerLoad == kChunk && BS % kRowsPerLoad == 0, "load tiling");
   // Three chunk buffers (K and V rows, [key][d], no padding; 16-byte columns
   // swizzled against bank conflicts, see below), filled by loads that write
-  // LDS directly: two chunks are in flight while a third is computed.
-  __shared__ __attribute__((aligned(16))) E lk0[kChunk * D], lv0[kChunk * D];
-  __shared__ __attribute__((aligned(16))) E lk1[kChunk * D], lv1[kChunk * D];
-  __shared__ __attribute__((aligned(16))) E lk2[kChunk * D], lv2[kChunk * D];
+  // LDS directly: two chunks are in flight while a third is computed.  One
+  // array (buffer b: K at ring[2 b], V at ring[2 b + 1]), so that every LDS
+  // read is a per-lane register plus a constant offset; separate arrays cost
+  // a register per buffer and operand (168 VGPRs against 144).
+  __shared__ __attribute__((aligned(16))) E ring[6][kChunk * D];
   __shared__ int sm_bad;
+  E* const lk0 = ring[0];
+  E* const lv0 = ring[1];
+  E* const lk1 = ring[2];
+  E* const lv1 = ring[3];
+  E* const lk2 = ring[4];
+  E* const lv2 = ring[5];
 
   // Linear id n: XCD x = n % 8 takes (sequence, head) pairs x, x + 8, ...
   // (pair = sequence * H + head); its r-th work-group (r = n / 8) is, in band

@@ -37,7 +37,7 @@ def test_header_declares_the_two_calls():
             "paged_attention_partition_size", "paged_kv_copy_blocks", "pkv_last_error", "pkv_pool_create",
             "pkv_pool_allocate", "pkv_pool_fork", "pkv_pool_append_slots", "pkv_pool_free",
             "pkv_pool_build_tables", "paged_attention_prefill", "paged_kv_prepare_step", "pkv_batch_plan_step",
-            "pkv_pool_usage", "paged_attention_decode_step", "pkv_read_probe"} <= set(fns)
+            "pkv_pool_usage", "paged_attention_decode_step", "pkv_read_probe", "pkv_mfma_probe"} <= set(fns)
 
 
 def test_library_exports_every_declared_function(libpath):
@@ -92,8 +92,18 @@ def rp(**kw):
     a.update(kw)
     return lib.pkv_read_probe(a["a"], a["b"], a["n"], a["tb"], a["o"], a["gl"], a["g"], a["gt"], a["depth"],
                               a["sink"], None)
+lib.pkv_mfma_probe.argtypes = [i32, i32, i32, i32, vp, vp, vp]
+def mp(**kw):
+    a = dict(dt=2, g=256, it=100, valu=0, sink=F, clk=None)
+    a.update(kw)
+    return lib.pkv_mfma_probe(a["dt"], a["g"], a["it"], a["valu"], a["sink"], a["clk"], None)
 ws = lib.paged_attention_workspace_bytes(64, 40, 128, 128, 16, 512)
 cases = [
+  ("mp_dtype_f32", lambda: mp(dt=0), 2), ("mp_dtype", lambda: mp(dt=9), 2), ("mp_groups", lambda: mp(g=0), 1),
+  ("mp_groups_high", lambda: mp(g=(1 << 20) + 1), 1), ("mp_iters", lambda: mp(it=0), 1),
+  ("mp_iters_high", lambda: mp(it=8001), 1), ("mp_valu", lambda: mp(valu=3), 2),
+  ("mp_null_sink", lambda: mp(sink=None), 1), ("mp_misaligned_sink", lambda: mp(sink=F + 2), 1),
+  ("mp_misaligned_clocks", lambda: mp(clk=F + 4), 1),
   ("dec_dtype", lambda: dec(dt=7), 2), ("dec_head_dim", lambda: dec(D=96), 2),
   ("dec_block", lambda: dec(bs=8), 2), ("dec_heads", lambda: dec(H=0), 1),
   ("dec_neg_seqs", lambda: dec(B=-1), 1), ("dec_zero_seqs", lambda: dec(B=0, q=None), 0),
