@@ -541,13 +541,18 @@ __global__ __launch_bounds__(64 * kWaves32) __attribute__((amdgpu_waves_per_eu(3
     if (pr >= num_heads * num_seqs) return;
     s = pr / num_heads;
     h = pr % num_heads;
-    tile = tiles - 1 - (klo + r % w);
+    tile = klo + r % w;                              // rank from the sequence's own last tile
   }
   const int qa = query_start[s], qb = query_start[s + 1];
   const int P = qb - qa;
   const int L = context_lens[s];
+  // Rank k is the sequence's k-th longest tile, so every pair's longest tile
+  // is in the first band and the ranks past a short sequence's tile count
+  // (work-groups with nothing to do) gather at the end of the grid.
+  const int ntiles = P > 0 ? min((P + kTileQ32 - 1) / kTileQ32, tiles) : 0;
+  if (tile >= ntiles) return;
+  tile = ntiles - 1 - tile;
   const int q0 = tile * kTileQ32;
-  if (P <= 0 || q0 >= P) return;
   const bool ok = P <= L && L <= max_blocks * BS && P <= tiles * kTileQ32;
   const int first = L - P;
   const int lane = threadIdx.x & 63;
