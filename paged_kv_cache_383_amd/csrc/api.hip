@@ -86,10 +86,11 @@ int32_t part_blocks_for(int32_t max_blocks, int32_t block_size, int32_t partitio
 // is fastest (no partials, no merge).  With fewer rows, contexts are cut into
 // partitions, multiples of kAutoGrain tokens, so that about
 // kAutoTargetGroups work-groups (about 5 per compute unit) cover the longest
-// possible context.  The grain keeps at least 4 stages per wave in a 16-token
-// block partition: with 512-token partitions each wave has 2, and the
-// work-group's fixed costs (merge, partial state, the reduce) dominate (one
-// sequence x 40 heads x 32k tokens: 126 us at 512, 109 us at 1024).
+// possible context.  Measured on 16-token blocks of 40 heads x 128 dims, one
+// sequence of 32k tokens takes 105.0 us at 512-token partitions, 105.9 at
+// 1024 (the split this picks), 108.3 at 2048 and 124.4 at 4096; four
+// sequences of 32k take 402.0 us at 4096 (picked) and 404.9 at 2048.  A
+// larger target would gain 1-2 % on the first shape and lose on the second.
 constexpr int64_t kAutoMinRows = 1024;
 constexpr int64_t kAutoTargetGroups = 1280;
 constexpr int64_t kAutoGrain = 1024;

@@ -12,7 +12,8 @@
 // FlashDecoding in "헷갈리기 쉬운 구분").
 //
 // Work decomposition.  One work-group of W wave64s (W = 8 for 16-token
-// blocks, 4 for 32-token blocks) per (head, partition, sequence); the grid's
+// blocks, 4 for 32-token blocks and for split partitions of at most 32
+// 16-token blocks) per (head, partition, sequence); the grid's
 // fastest index is the head, so work-groups running together read
 // neighbouring (block, head) tiles of the same physical blocks.  A wave works
 // in stages of TPS consecutive blocks (one 32-token or two 16-token bf16/fp16
@@ -66,6 +67,9 @@ template <int BS>
 constexpr int waves_for() {
   return BS == 16 ? 8 : 4;
 }
+// Split partitions of at most this many blocks run 4-wave work-groups (see
+// launch_typed).
+constexpr int kSmallPartitionBlocks = 32;
 // Running max before any token is seen.  Finite, so 2^(m - m') is defined
 // while a row has seen only masked tokens; any real score exceeds it.
 constexpr float kEmptyMax = -3.0e38f;
@@ -537,7 +541,20 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   constexpr int kNst = stages_for<DT, kTps>();
   auto* kernel = a.k_new != nullptr ? decode_partition_kernel<DT, D, BS, kWaves, kTps, kNst, true>
                                     : decode_partition_kernel<DT, D, BS, kWaves, kTps, kNst, false>;
-  hipLaunchKernelGGL(kernel, grid, dim3(64 * kWaves), 0, stream, a.q,
+  int waves = kWaves;
+  // Partitions of at most 32 blocks (512 tokens of 16-token blocks) give an
+  // 8-wave work-group only two stages per wave; 4-wave work-groups (the same
+  // per-wave pipeline, two of them per compute unit) overlap one's start and
+  // merge with the other's loads (8 x 40 x 32k at 512-token partitions: 857
+  // vs 876 us per step).
+  if constexpr (kWaves == 8) {
+    if (a.partitions > 1 && a.part_blocks <= kSmallPartitionBlocks) {
+      kernel = a.k_new != nullptr ? decode_partition_kernel<DT, D, BS, 4, kTps, kNst, true>
+                                  : decode_partition_kernel<DT, D, BS, 4, kTps, kNst, false>;
+      waves = 4;
+    }
+  }
+  hipLaunchKernelGGL(kernel, grid, dim3(64 * waves), 0, stream, a.q,
                      static_cast<char*>(a.k_cache), static_cast<char*>(a.v_cache),
                      a.block_tables, a.context_lens, a.out, a.ws_m, a.ws_l, a.ws_acc, a.num_blocks,
                      a.max_blocks, a.part_blocks, a.partitions, a.scale_log2,
