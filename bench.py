@@ -21,7 +21,7 @@ Prints one JSON line:
 Timing: the K steps run back to back with no event between them (wall clock and one HIP event
 pair bracket them); then the other form of the step, the decode call alone and the write alone
 run K times back to back, each bracketed by a HIP event pair, for the per-launch averages.
-Other workloads (--workload): parallel_sampling, continuous_batching, prefill.
+Other workloads (--workload): parallel_sampling, continuous_batching, prefill, split_sweep.
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--config 2]
 """
 from __future__ import annotations
