@@ -87,10 +87,9 @@ int32_t part_blocks_for(int32_t max_blocks, int32_t block_size, int32_t partitio
 // partitions, multiples of kAutoGrain tokens, so that about
 // kAutoTargetGroups work-groups (about 5 per compute unit) cover the longest
 // possible context.  Measured on 16-token blocks of 40 heads x 128 dims, one
-// sequence of 32k tokens takes 105.0 us at 512-token partitions, 105.9 at
-// 1024 (the split this picks), 108.3 at 2048 and 124.4 at 4096; four
-// sequences of 32k take 402.0 us at 4096 (picked) and 404.9 at 2048.  A
-// larger target would gain 1-2 % on the first shape and lose on the second.
+// sequence of 32k tokens takes 104.7 us at 512-token partitions, 103.7 at
+// 1024 (the split this picks), 108.3 at 2048 and 123.5 at 4096; four
+// sequences of 32k take 400.1 us at 4096 (picked) and 402.0 at 2048.
 constexpr int64_t kAutoMinRows = 1024;
 constexpr int64_t kAutoTargetGroups = 1280;
 constexpr int64_t kAutoGrain = 1024;

@@ -12,7 +12,7 @@
 // FlashDecoding in "헷갈리기 쉬운 구분").
 //
 // Work decomposition.  One work-group of W wave64s (W = 8 for 16-token
-// blocks, 4 for 32-token blocks and for split partitions of at most 32
+// blocks, 4 for 32-token blocks and for split partitions of at most 64
 // 16-token blocks) per (head, partition, sequence); the grid's
 // fastest index is the head, so work-groups running together read
 // neighbouring (block, head) tiles of the same physical blocks.  A wave works
@@ -69,7 +69,7 @@ constexpr int waves_for() {
 }
 // Split partitions of at most this many blocks run 4-wave work-groups (see
 // launch_typed).
-constexpr int kSmallPartitionBlocks = 32;
+constexpr int kSmallPartitionBlocks = 64;
 // Running max before any token is seen.  Finite, so 2^(m - m') is defined
 // while a row has seen only masked tokens; any real score exceeds it.
 constexpr float kEmptyMax = -3.0e38f;
@@ -542,11 +542,12 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   auto* kernel = a.k_new != nullptr ? decode_partition_kernel<DT, D, BS, kWaves, kTps, kNst, true>
                                     : decode_partition_kernel<DT, D, BS, kWaves, kTps, kNst, false>;
   int waves = kWaves;
-  // Partitions of at most 32 blocks (512 tokens of 16-token blocks) give an
-  // 8-wave work-group only two stages per wave; 4-wave work-groups (the same
-  // per-wave pipeline, two of them per compute unit) overlap one's start and
-  // merge with the other's loads (8 x 40 x 32k at 512-token partitions: 857
-  // vs 876 us per step).
+  // Partitions of at most 64 blocks (1024 tokens of 16-token blocks) give an
+  // 8-wave work-group at most four stages per wave; 4-wave work-groups (the
+  // same per-wave pipeline, two of them per compute unit) overlap one's start
+  // and merge with the other's loads (8 x 40 x 32k at 512-token partitions:
+  // 857 vs 876 us per step; 1 x 40 x 32k at 1024-token partitions: 103.7 vs
+  // 105.7 us per call).  At 128 blocks they lose on some shapes.
   if constexpr (kWaves == 8) {
     if (a.partitions > 1 && a.part_blocks <= kSmallPartitionBlocks) {
       kernel = a.k_new != nullptr ? decode_partition_kernel<DT, D, BS, 4, kTps, kNst, true>
