@@ -821,6 +821,9 @@ def main():
     ap.add_argument("--partition-size", type=int, default=None,
                     help="split-context partition in tokens (0 = one pass); default: the library's choice")
     ap.add_argument("--rotate", type=int, default=None, help="independent input copies cycled over")
+    ap.add_argument("--placement", choices=["shuffled", "consecutive"], default="shuffled",
+                    help="decode: block ids from the shuffled free list (default) or one consecutive run per "
+                         "sequence (same lengths and bytes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-diagnostic", action="store_true",
                     help="skip the read-probe and matrix-core-probe ceilings and the PyTorch streaming figures (counter runs)")
@@ -862,7 +865,7 @@ def main():
         return
 
     dev = torch.device("cuda:0")
-    meta = W.make_metadata(args.config)
+    meta = W.make_metadata(args.config, placement=args.placement)
     cfg = meta.cfg
     part = pkv.PARTITION_AUTO if args.partition_size is None else args.partition_size
     resolved = pkv.paged_attention_partition_size(len(meta.context_lens), cfg.num_heads, cfg.max_blocks,
@@ -986,7 +989,7 @@ def main():
         cpu = cpu_baseline(meta, sets[0])
         log(f"cpu oracle: {cpu}")
 
-    traffic = measured_traffic(cfg.name, resolved)
+    traffic = measured_traffic(cfg.name, resolved) if args.placement == "shuffled" else None
     th = meta.total_tokens * cfg.num_heads
     rec = {
         "metric": METRIC,
@@ -1009,6 +1012,7 @@ def main():
             "block_size": cfg.block_size,
             "sum_context_tokens": meta.total_tokens,
             "pool_blocks": meta.num_blocks,
+            "block_placement": args.placement,
             "partition_size": resolved,
             "partition_choice": "library (PKV_PARTITION_AUTO)" if part == pkv.PARTITION_AUTO else "caller",
             "step": ("paged_kv_write(one new token per sequence) + paged_attention_decode" if args.two_call_step

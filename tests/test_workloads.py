@@ -57,6 +57,21 @@ def test_lengths_follow_each_distribution():
     assert L5.min() >= 16 and L5.max() <= 4096
 
 
+@pytest.mark.parametrize("cfg_id", [2, 4])
+def test_consecutive_placement_changes_only_block_ids(cfg_id):
+    a, b = W.make_metadata(cfg_id), W.make_metadata(cfg_id, placement="consecutive")
+    assert np.array_equal(a.context_lens, b.context_lens) and a.num_blocks == b.num_blocks
+    assert (a.block_tables >= 0).sum() == (b.block_tables >= 0).sum()
+    assert np.array_equal(a.block_tables >= 0, b.block_tables >= 0)
+    assert np.array_equal(a.owner == W.FOREIGN, b.owner == W.FOREIGN)
+    ids = np.concatenate([row[row >= 0] for row in b.block_tables])
+    assert (np.diff(ids) > 0).all()                          # ascending through the batch
+    if cfg_id == 2:                                          # no foreign blocks: one run from block 0
+        assert np.array_equal(ids, np.arange(len(ids)))
+    with pytest.raises(ValueError):
+        W.make_metadata(cfg_id, placement="interleaved")
+
+
 def test_seeded_and_reproducible():
     a, b = W.make_metadata(2), W.make_metadata(2)
     assert np.array_equal(a.block_tables, b.block_tables) and np.array_equal(a.context_lens, b.context_lens)

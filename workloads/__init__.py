@@ -127,14 +127,23 @@ def _pool_and_free_list(cfg: Config, needed: int, rng: np.random.Generator):
     return nb, free, foreign
 
 
-def make_metadata(cfg: Config | int, lens: np.ndarray | None = None, seed: int | None = None) -> Metadata:
+PLACEMENTS = ("shuffled", "consecutive")
+
+
+def make_metadata(cfg: Config | int, lens: np.ndarray | None = None, seed: int | None = None,
+                  placement: str = "shuffled") -> Metadata:
     """Context lengths, pool, tables and newest-token slots for one decode step.
 
     Tables take block ids from the shuffled free list in batch order, one id per
     ``block_size`` tokens (the pages' on-demand allocation: a sequence holds
     exactly ceil(L / block_size) blocks).  ``lens`` overrides the drawn lengths
-    (the pool is then sized by the same per-config rule).
+    (the pool is then sized by the same per-config rule).  ``placement =
+    "consecutive"`` sorts the free list instead, so each sequence holds a run of
+    consecutive block ids (same lengths, pool and bytes; the random draws are
+    the same, so only the placement differs).
     """
+    if placement not in PLACEMENTS:
+        raise ValueError(f"placement must be one of {PLACEMENTS}")
     if isinstance(cfg, int):
         cfg = CONFIGS[cfg]
     seed = SEED_BASE + cfg.cfg_id if seed is None else seed
@@ -147,6 +156,8 @@ def make_metadata(cfg: Config | int, lens: np.ndarray | None = None, seed: int |
     nblk = (L + bs - 1) // bs
     needed = int(nblk.sum())
     nb, free, foreign = _pool_and_free_list(cfg, needed, rng)
+    if placement == "consecutive":
+        free = np.sort(free)
     if len(free) < needed:
         raise ValueError("pool too small for the requested lengths")
     B = len(L)
