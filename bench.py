@@ -821,6 +821,9 @@ def main():
     ap.add_argument("--partition-size", type=int, default=None,
                     help="split-context partition in tokens (0 = one pass); default: the library's choice")
     ap.add_argument("--rotate", type=int, default=None, help="independent input copies cycled over")
+    ap.add_argument("--block-size", type=int, choices=[16, 32], default=None,
+                    help="decode: store the configuration's context lengths in blocks of this many tokens "
+                         "instead of its own block size (same lengths and bytes)")
     ap.add_argument("--placement", choices=["shuffled", "consecutive"], default="shuffled",
                     help="decode: block ids from the shuffled free list (default) or one consecutive run per "
                          "sequence (same lengths and bytes)")
@@ -865,7 +868,12 @@ def main():
         return
 
     dev = torch.device("cuda:0")
-    meta = W.make_metadata(args.config, placement=args.placement)
+    base_cfg = W.CONFIGS[args.config]
+    if args.block_size and args.block_size != base_cfg.block_size:
+        import dataclasses
+        name = base_cfg.name.replace(f"_bs{base_cfg.block_size}", "") + f"_bs{args.block_size}"
+        base_cfg = dataclasses.replace(base_cfg, block_size=args.block_size, name=name)
+    meta = W.make_metadata(base_cfg, placement=args.placement)
     cfg = meta.cfg
     part = pkv.PARTITION_AUTO if args.partition_size is None else args.partition_size
     resolved = pkv.paged_attention_partition_size(len(meta.context_lens), cfg.num_heads, cfg.max_blocks,
