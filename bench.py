@@ -151,6 +151,48 @@ def cpu_baseline(meta, w, budget_s=12.0, single_s=4.0):
             **cpu_host_info()}
 
 
+def cpu_oracle_steps(q, k0, v0, kn, vn, tables, lens, slots, scale, bs, dtype, step_bytes, copies=None,
+                     budget_s=12.0, what="one step"):
+    """Whole steps of a decode workload by the oracle, untouched, on the host's cores: the oracle's block copies
+    (when ``copies`` is given), its write of the new tokens (a copy of the whole pool) and oracle.decode of every
+    row, the rows shared out to a pool of threads as in cpu_baseline, until about budget_s.  ``step_bytes`` is
+    the GPU step's algorithmic byte count, so the rate is in the workload's own unit."""
+    import resource
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    from oracle import block_manager
+    L = np.asarray(lens).astype(np.int64)
+    H = q.shape[1]
+    order = np.argsort(-L, kind="stable").tolist()
+    order = [i for i in order if L[i] > 0]
+    nw = cpu_workers()
+
+    def one(args):
+        kc, vc, i = args
+        oracle.decode(q, kc, vc, tables, lens, scale, bs, dtype, seqs=[i])
+
+    steps = 0
+    cpu0 = resource.getrusage(resource.RUSAGE_SELF)
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(nw) as ex:
+        while steps == 0 or time.perf_counter() - t0 < budget_s:
+            kc, vc = (block_manager.copy_blocks(k0, v0, copies) if copies is not None and len(copies)
+                      else (k0, v0))
+            kc, vc = oracle.kv_write(kn, vn, slots, kc, vc, bs)
+            list(ex.map(one, [(kc, vc, i) for i in order]))
+            steps += 1
+    wall = time.perf_counter() - t0
+    cpu1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (cpu1.ru_utime - cpu0.ru_utime) + (cpu1.ru_stime - cpu0.ru_stime)
+    return {"value": round(steps * step_bytes / wall / 1e9, 4), "unit": "GB/s", "cores": nw, "kind": "oracle",
+            "sample": f"{steps} x ({what}), {len(order)} rows each, on {nw} threads; {wall:.1f} s wall, "
+                      f"{cpu:.1f} s CPU ({cpu / wall:.1f} cores busy on average)",
+            "tokens_heads_per_s": round(steps * int(L.sum()) * H / wall, 1), **cpu_host_info()}
+
+
 def cpu_baseline_prefill(q, kc, vc, tables, lens, scale, bs, dtype, budget_s=12.0):
     """The oracle's prefill, untouched, on the same prompts and the host's cores: each prompt's queries over its
     own cache blocks, prompts shared out to a pool of threads (as for the decode baseline), new prompts
@@ -475,6 +517,14 @@ def parallel_sampling(args):
         "unique_kv_bytes": unique_b,
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        st = sets[0]
+        rec["cpu_baseline"] = cpu_oracle_steps(
+            W.storage_numpy(st["q"]), W.storage_numpy(st["kc"]), W.storage_numpy(st["vc"]),
+            W.storage_numpy(st["kn"]), W.storage_numpy(st["vn"]), tab0, st["ctx"], st["slots"].cpu().numpy(),
+            cfg.scale, bs, cfg.dtype, step_b, copies=st["copies"].cpu().numpy().tolist(),
+            what="the step's block copies, its write of the new tokens and its decode")
+        log(f"cpu oracle: {rec['cpu_baseline']}")
     print(json.dumps(rec), flush=True)
 
 
@@ -594,6 +644,24 @@ def continuous_batching(args):
                      "algorithmic_bytes_per_launch": decode_b, "mean_launch_us": round(decode_us, 2)},
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        # the oracle on the loop's final batch: whole steps of its write of the running rows' new tokens and
+        # its decode of every running row, over a pool of just the blocks the batch holds (ids renumbered)
+        import oracle
+        tab = loop.tables.cpu().numpy().astype(np.int64)
+        lens_h = loop.lens.cpu().numpy()
+        used = np.unique(tab[tab >= 0])
+        renum = np.full(NB, -1, dtype=np.int64)
+        renum[used] = np.arange(len(used))
+        tab_c = np.where(tab >= 0, renum[np.maximum(tab, 0)], -1).astype(np.int32)
+        idx = torch.from_numpy(used).to(dev)
+        active = int((lens_h > 0).sum())
+        rec["cpu_baseline"] = cpu_oracle_steps(
+            W.storage_numpy(q), W.storage_numpy(kc.index_select(0, idx)), W.storage_numpy(vc.index_select(0, idx)),
+            W.storage_numpy(kn), W.storage_numpy(vn), tab_c, lens_h, oracle.newest_token_slots(tab_c, lens_h, bs),
+            loop.scale, bs, cfg.dtype, decode_b + active * 4 * row_b + 8 * active,
+            what="the loop's final batch: its write of the running rows' new tokens and its decode")
+        log(f"cpu oracle: {rec['cpu_baseline']}")
     print(json.dumps(rec), flush=True)
 
 
