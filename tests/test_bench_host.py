@@ -60,3 +60,25 @@ def test_more_than_one_gpu_is_refused():
                          text=True, timeout=120)
     assert res.returncode != 0
     assert "one GPU" in (res.stdout + res.stderr)
+
+
+def test_cpu_oracle_steps_runs_whole_oracle_steps():
+    """The CPU baseline of the secondary workloads: whole oracle steps (block copies, write, decode) on a tiny
+    batch, its rate in the caller's byte count, every row with a context counted once per step."""
+    import numpy as np
+    rng = np.random.default_rng(7)
+    H, D, bs, NB = 2, 64, 16, 12
+    k0 = rng.standard_normal((NB, H, bs, D)).astype(np.float32)
+    v0 = rng.standard_normal((NB, H, bs, D)).astype(np.float32)
+    tables = np.array([[0, 1, -1], [2, -1, -1], [-1, -1, -1]], dtype=np.int32)
+    lens = np.array([20, 5, 0], dtype=np.int32)                  # the empty row is skipped
+    q = rng.standard_normal((3, H, D)).astype(np.float32)
+    kn = rng.standard_normal((3, H, D)).astype(np.float32)
+    vn = rng.standard_normal((3, H, D)).astype(np.float32)
+    slots = np.array([1 * bs + 3, 2 * bs + 4, -1], dtype=np.int64)
+    r = bench.cpu_oracle_steps(q, k0, v0, kn, vn, tables, lens, slots, 0.125, bs, "f32", step_bytes=10**6,
+                               copies=[[2, 5]], budget_s=0.2, what="a test step")
+    steps = int(r["sample"].split(" x ")[0])
+    assert steps >= 1 and r["kind"] == "oracle" and r["unit"] == "GB/s" and r["cores"] >= 1
+    assert r["tokens_heads_per_s"] > 0 and r["value"] > 0
+    assert "2 rows each" in r["sample"] and "a test step" in r["sample"]
